@@ -1,0 +1,244 @@
+"""Benchmark of the paged attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload headline|1..5] [--no-cpu-baseline]
+
+One step runs every call of the selected workloads once, inputs already
+resident in HBM (the pool write is setup and is not timed).  The default
+"headline" step is the 4 x 4096 causal prefill (bf16, 32 q / 8 KV heads,
+d=128) followed by the 8 x 32768 long-context decode (bf16, 64 q / 8 KV heads,
+d=128, split-KV + logsumexp merge).  Prints one JSON line:
+  value     prefill TFLOP/s (4*d FLOPs per visible query-key pair per q head)
+  decode    KV GB/s of the decode calls (K+V bytes read, logical)
+  roofline  of the prefill kernel (MFMA bound), roofline_decode of the decode
+  cpu_baseline  the float64 oracle timed on a bounded sample on the host.
+Per-kernel times come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+METRIC = "prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 1 MI355X"
+
+
+def prefill_flops(call, head_dim, num_q_heads) -> float:
+    """4*d FLOPs (QK^T and PV) for every visible (query, key) pair, per q head."""
+    total = 0
+    for b, q in enumerate(call.q_lens):
+        c = int(call.ctx_lens[b])
+        if call.causal:
+            # query i sits at c - q + i and sees c - q + i + 1 keys
+            total += q * (c - q) + q * (q + 1) // 2
+        else:
+            total += q * c
+    return 4.0 * head_dim * num_q_heads * total
+
+
+def decode_kv_bytes(call, wl) -> float:
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    toks = int(call.ctx_lens.sum())
+    return float(toks) * wl.num_kv_heads * wl.head_dim * 2 * elem
+
+
+def _src_hash(name: str) -> str:
+    p = os.path.join(ROOT, "online_softmax_paged_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_file: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current source of the kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    rec = data.get(f"{kernel_file}:{workload}")
+    if not rec or rec.get("source_sha") != _src_hash(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wls, budget_s: float):
+    """Time the float64 oracle on a bounded sample of the same workloads."""
+    import numpy as np
+    import torch
+
+    from oracle import OraclePool, write_kv, gather_kv, attention_two_pass
+
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    out = {}
+    for wl in wls:
+        opool = OraclePool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+        write_kv(opool, wl.k_src, wl.v_src, wl.slot_mapping)
+        G = wl.num_q_heads // wl.num_kv_heads
+        for call in wl.calls:
+            work, n_units, t_used = 0.0, 0, 0.0
+            cu = call.cu_q_lens.tolist()
+            units = [(b, h) for b in range(len(call.seqs)) for h in range(wl.num_q_heads)]
+            t0 = time.perf_counter()
+            for (b, h) in units:
+                c = int(call.ctx_lens[b])
+                K, V = gather_kv(opool, call.block_table[b], c, h // G)
+                q = call.q[cu[b]:cu[b + 1], h] if call.kind == "prefill" else call.q[b:b + 1, h]
+                nq = q.shape[0]
+                pos = np.arange(c - nq, c)
+                attention_two_pass(q, K, V, wl.scale, pos, call.causal)
+                if call.kind == "prefill":
+                    vis = nq * (c - nq) + nq * (nq + 1) // 2 if call.causal else nq * c
+                    work += 4.0 * wl.head_dim * vis
+                else:
+                    work += c * wl.head_dim * 2 * {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype] / G
+                n_units += 1
+                t_used = time.perf_counter() - t0
+                if t_used > budget_s / max(1, sum(len(w.calls) for w in wls)):
+                    break
+            unit = "TFLOP/s" if call.kind == "prefill" else "GB/s"
+            rate = work / t_used / (1e12 if call.kind == "prefill" else 1e9)
+            out[call.kind] = {"value": rate, "unit": unit, "cores": cores, "kind": "oracle",
+                              "sample": f"{n_units} of {len(units)} (sequence, q-head) rows of "
+                                        f"{wl.name} {call.kind}, {t_used:.1f} s"}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence and KV head, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import online_softmax_paged_amd as pa
+    import workloads
+
+    if args.workload == "headline":
+        wls = [workloads.causal_prefill_bf16(), workloads.long_decode_bf16()]
+    else:
+        wls = [workloads.NAMED[int(args.workload)]()]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    launches = []   # (kind, wl, fn)
+    for wl in wls:
+        pool = pa.KVPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, device=dev)
+        pa.write_kv(pool, wl.k_src.to(dev), wl.v_src.to(dev), wl.slot_mapping.to(dev))
+        for call in wl.calls:
+            q = call.q.to(dev)
+            cu, ctx, bt = call.cu_q_lens.to(dev), call.ctx_lens.to(dev), call.block_table.to(dev)
+            mq, mc = max(call.q_lens), int(call.ctx_lens.max())
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+            if call.kind == "prefill":
+                fn = (lambda pool=pool, q=q, cu=cu, ctx=ctx, bt=bt, mq=mq, mc=mc, o=o, lse=lse, wl=wl, c=call:
+                      pa.prefill(pool, q, cu, ctx, bt, wl.scale, causal=c.causal, max_q_len=mq,
+                                 max_ctx_len=mc, out=o, lse=lse))
+            else:
+                B, Hq, D = q.shape
+                S = pa.decode_num_splits(B, wl.num_kv_heads, mc)
+                ws = torch.empty(max(1, pa.decode_workspace_bytes(B, Hq, D, S)), dtype=torch.uint8, device=dev)
+                fn = (lambda pool=pool, q=q, ctx=ctx, bt=bt, mc=mc, o=o, lse=lse, wl=wl, ws=ws, S=S:
+                      pa.decode(pool, q, ctx, bt, wl.scale, max_ctx_len=mc, num_splits=S,
+                                workspace=ws, out=o, lse=lse))
+            launches.append((call.kind, wl, call, fn))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for _, _, _, fn in launches:
+            fn()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in launches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, _, _, fn) in enumerate(launches):
+            evs[s][i][0].record()
+            fn()
+            evs[s][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_launch_ms = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)) / args.steps
+                     for i in range(len(launches))]
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)"}
+    parts = {}
+    for (kind, wl, call, _), ms in zip(launches, per_launch_ms):
+        if kind == "prefill":
+            fl = prefill_flops(call, wl.head_dim, wl.num_q_heads)
+            tf = fl / (ms * 1e-3) / 1e12
+            peak = PEAK_BF16_TFLOPS
+            parts.setdefault("prefill", []).append(
+                {"workload": wl.name, "ms": ms, "tflops": tf, "frac_bf16_peak": tf / peak,
+                 "flops": fl, "dtype": wl.kv_dtype})
+        else:
+            by = decode_kv_bytes(call, wl)
+            gbps = by / (ms * 1e-3) / 1e9
+            parts.setdefault("decode", []).append(
+                {"workload": wl.name, "ms": ms, "gbps": gbps, "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
+                 "kv_bytes": by, "dtype": wl.kv_dtype})
+    pre = parts.get("prefill", [])
+    dec = parts.get("decode", [])
+    if pre:
+        fl = sum(p["flops"] for p in pre)
+        ms = sum(p["ms"] for p in pre)
+        result["value"] = fl / (ms * 1e-3) / 1e12
+        result["unit"] = "TFLOP/s"
+    else:
+        by = sum(d["kv_bytes"] for d in dec)
+        ms = sum(d["ms"] for d in dec)
+        result["value"] = by / (ms * 1e-3) / 1e9
+        result["unit"] = "GB/s"
+    result["dtype"] = "bf16" if all(w.kv_dtype == "bf16" for w in wls) else \
+        "+".join(sorted({("bf16-q/fp8-kv" if w.kv_dtype == "fp8" else w.kv_dtype) for w in wls}))
+    result["config"] = {"workload": " + ".join(w.name for w in wls)}
+    if pre:
+        p = pre[0]
+        result["roofline"] = {"bound": "mfma", "achieved": p["tflops"], "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": p["tflops"] / PEAK_BF16_TFLOPS,
+                              "traffic": traffic_for("prefill.hip", p["workload"])}
+    if dec:
+        d = dec[0]
+        key = "roofline_decode" if pre else "roofline"
+        result[key] = {"bound": "hbm", "achieved": d["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                       "frac": d["gbps"] / PEAK_HBM_GBPS,
+                       "traffic": traffic_for("decode.hip", d["workload"])}
+        result["decode"] = {"value": sum(x["kv_bytes"] for x in dec) / (sum(x["ms"] for x in dec) * 1e-3) / 1e9,
+                            "unit": "GB/s", "frac_hbm_peak": None}
+        result["decode"]["frac_hbm_peak"] = result["decode"]["value"] / PEAK_HBM_GBPS
+    result["parts"] = parts
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wls, args.cpu_budget)
+        first = cb.get("prefill") or cb.get("decode")
+        result["cpu_baseline"] = dict(first)
+        if "prefill" in cb and "decode" in cb:
+            result["cpu_baseline"]["decode"] = cb["decode"]
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * pa.h -- paged attention forward for MI355X (gfx950): C ABI.
+ *
+ * Exact scaled-dot-product attention, softmax(scale * Q K^T) V, computed with
+ * K/V tiles streamed from a paged KV cache and an online softmax (running max,
+ * running sum, rescaled accumulator; the logsumexp is written out).
+ *
+ * Sources of the operations (web pages on FlashAttention and PagedAttention):
+ *  - the attention itself: the FlashAttention/PagedAttention survey page
+ *    ("FlashAttention与PagedAttention技术详解"), section 1, scaled dot-product
+ *    self-attention with d_k the head dimension;
+ *  - tiling, safe softmax and the kept statistics (max and logsumexp): the same
+ *    page, section 2, "core principle"; FlashAttention-2 keeps only logsumexp
+ *    (section 2, FlashAttention-2 improvements);
+ *  - the paged KV cache: fixed 16-token physical blocks, a per-sequence block
+ *    table mapping logical to physical blocks, blocks allocated on demand and
+ *    freed when a request ends, and reference-counted sharing of a common
+ *    prompt's blocks: the same page, section 3, "core principle", and the
+ *    "core modules" chapter page, section 2.2 (its pseudocode loops over a
+ *    sequence's logical blocks, looks up the physical block and merges each
+ *    block's scores into running statistics).
+ *
+ * Conventions common to every entry point:
+ *  - Device pointers are plain device addresses (e.g. from hipMalloc or a torch
+ *    CUDA tensor's data_ptr()); the caller owns every buffer.  The library never
+ *    allocates, frees or synchronises device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it; calls return before the work is done.
+ *  - Arguments that live on the host are checked before anything is enqueued;
+ *    a failed check returns a negative pa_status and enqueues nothing.  A launch
+ *    failure returns PA_ERR_LAUNCH.  No C++ exception crosses this boundary.
+ *  - Metadata that lives on the device (lengths, block tables, slot mappings)
+ *    is not read by the host.  The caller guarantees: 1 <= q_len_b <= ctx_len_b
+ *    <= max_ctx_len, q_len_b <= max_q_len, and block_table[b][j] in
+ *    [0, num_blocks) for every j < ceil(ctx_len_b / 16).  Entries past that are
+ *    never read.  A block id outside [0, num_blocks) is never dereferenced (the
+ *    page is treated as empty), but the result is then unspecified.
+ *  - Calls are reentrant; the library keeps no mutable global state.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad alignment          */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype / head_dim / group  */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  PA_ERR_OOM = -4,         /* host block allocator has no free block         */
+  PA_ERR_LAUNCH = -5       /* a HIP launch or runtime call failed            */
+} pa_status;
+
+typedef enum {
+  PA_F32 = 0,      /* IEEE binary32                                          */
+  PA_BF16 = 1,     /* bfloat16                                               */
+  PA_FP8_E4M3 = 2  /* OCP E4M3FN: bias 7, max +-448, NaN = S.1111.111; pool only */
+} pa_dtype;
+
+/*
+ * The KV block pool (caller-owned device memory).
+ *   k: [num_blocks, num_kv_heads, 16, head_dim]  token-major inside a page
+ *   v: [num_blocks, num_kv_heads, head_dim, 16]  feature-major inside a page
+ * Each (physical block, KV head) is one contiguous chunk of 16 * head_dim
+ * elements (4 KiB for bf16 and head_dim 128).  Keeping V feature-major inside
+ * the page lets the P.V product read its operand as 16-byte runs of keys.
+ * For PA_FP8_E4M3 pools, k_scale/v_scale hold one float per physical block,
+ * shared by all KV heads: stored value = code * scale.  Otherwise they are
+ * ignored (may be NULL).  k and v must be 16-byte aligned.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;    /* 64 or 128 */
+  int32_t block_size;  /* must be 16 */
+  pa_dtype kv_dtype;
+} pa_kv_pool;
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Version of this ABI (incremented on any signature or layout change). */
+int32_t pa_abi_version(void);
+
+/* ------------------------------------------------------------------ write
+ * Scatter num_tokens new tokens into the pool (on-demand block use, as the
+ * survey page's section 3 describes for newly generated tokens).
+ *   k_new, v_new : [num_tokens, num_kv_heads, head_dim] in src_dtype (device)
+ *   slot_mapping : int32 [num_tokens] (device); token t goes to physical block
+ *                  slot_mapping[t] / 16, offset slot_mapping[t] % 16
+ * Pool f32 <- src f32, pool bf16 <- src bf16: exact copy.
+ * Pool fp8 <- src f32 or bf16: every block touched by this call gets one K and
+ *   one V scale, s = amax / 448 (float32, correctly rounded; s = 1 when amax is
+ *   0) where amax is the largest |value| this call writes into that block (all
+ *   heads, dims, tokens), and each value becomes the nearest-even E4M3 code of
+ *   clamp(x / s, -448, 448).  So a block must be written whole by one call;
+ *   earlier codes of a block touched again are not re-quantised.
+ * workspace: device memory of pa_write_kv_workspace_bytes(pool) bytes
+ *   (0 for non-fp8 pools; may then be NULL).  Slots must be distinct.
+ */
+size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool);
+pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ gather
+ * Copy each sequence's logical tokens out of the pool, through its block
+ * table, into contiguous token-major buffers (bit-exact copy of the stored
+ * bytes; fp8 codes are copied without scaling).  Used to check the pool and
+ * block-table addressing and as a bandwidth probe.
+ *   block_table : int32 [num_seqs, bt_stride] (device)
+ *   ctx_lens    : int32 [num_seqs] (device)
+ *   cu_ctx      : int32 [num_seqs + 1] (device), prefix sums of ctx_lens
+ *   k_out, v_out: [cu_ctx[num_seqs], num_kv_heads, head_dim] pool dtype (device)
+ * max_ctx_len bounds every ctx_lens entry.
+ */
+pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* ctx_lens, const int32_t* cu_ctx, int32_t num_seqs,
+                       int32_t max_ctx_len, void* k_out, void* v_out, void* stream);
+
+/* ------------------------------------------------------------------ prefill
+ * Causal (or full) attention of a batch of query chunks against the paged
+ * cache.  Sequence b has q_len_b = cu_q_lens[b+1] - cu_q_lens[b] query tokens
+ * that are the LAST q_len_b of its ctx_len_b cached tokens (their K/V must
+ * already be in the pool): query i of sequence b sits at position
+ * ctx_len_b - q_len_b + i and, when causal, sees keys 0..that position.
+ *   q   : [cu_q_lens[num_seqs], num_q_heads, head_dim], q_dtype (device)
+ *   o   : same shape, q_dtype (device, written)
+ *   lse : float [cu_q_lens[num_seqs], num_q_heads] natural-log logsumexp of the
+ *         scaled scores of each row (device, written; may be NULL)
+ *   cu_q_lens : int32 [num_seqs + 1]; ctx_lens : int32 [num_seqs] (device)
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Supported: q_dtype PA_F32 with an f32 pool; q_dtype PA_BF16 with a bf16 or
+ * fp8 pool.  head_dim 64 or 128; num_q_heads / num_kv_heads in {1,2,4,8,16}.
+ * q and o must be 16-byte aligned.
+ */
+pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                     float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                     const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                     float scale, int32_t causal, void* stream);
+
+/* ------------------------------------------------------------------ decode
+ * One query token per sequence, at position ctx_len_b - 1 (it sees all
+ * ctx_len_b cached keys).  Split-KV: each sequence's pages are cut into
+ * num_splits contiguous page ranges; one pass computes, per (sequence, KV head,
+ * range), the normalised partial output and logsumexp of all the group's query
+ * heads into the workspace, and a second pass merges the ranges by their
+ * logsumexps:  lse = M + ln sum_s exp(lse_s - M),  o = sum_s exp(lse_s - lse) o_s.
+ * (The merge is the same combination of partial softmax statistics that the
+ * online softmax applies block by block, "core modules" chapter, section 2.1.)
+ *   q   : [num_seqs, num_q_heads, head_dim], q_dtype (device)
+ *   o   : same shape and dtype (device, written)
+ *   lse : float [num_seqs, num_q_heads] (device, written; may be NULL)
+ * num_splits: 0 = choose with pa_decode_num_splits(); 1 = no merge pass, no
+ *   workspace needed.  workspace: device memory of at least
+ *   pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, splits) bytes,
+ *   16-byte aligned, contents need not be initialised.  Same dtype and group
+ *   support as pa_prefill.
+ */
+int32_t pa_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t num_splits);
+pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                    float* lse, const int32_t* ctx_lens, const int32_t* block_table,
+                    int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_ctx_len, float scale, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ blocks
+ * Host-side block allocator for a pool of num_blocks physical blocks: a free
+ * list plus one reference count per block (survey page section 3: on-demand
+ * allocation, freeing at request end, reference counts for blocks shared by
+ * sequences with a common prompt).  Not thread-safe; one allocator per pool.
+ *   pa_alloc_block      : a free block with refcount 1, or -1 when none is free
+ *                         (lowest free id first, so allocation is deterministic)
+ *   pa_block_incref     : one more owner of an allocated block (sharing)
+ *   pa_block_decref     : one owner fewer; the block is free again at 0.
+ *                         PA_ERR_INVALID_ARG on a free block (double free) or a
+ *                         bad id.
+ *   pa_block_refcount   : current count (0 = free), -1 for a bad id
+ *   pa_num_free_blocks  : number of free blocks
+ */
+typedef struct pa_allocator pa_allocator;
+pa_allocator* pa_allocator_create(int32_t num_blocks);  /* NULL if num_blocks < 1 */
+void pa_allocator_destroy(pa_allocator* a);
+int32_t pa_alloc_block(pa_allocator* a);
+pa_status pa_block_incref(pa_allocator* a, int32_t block);
+pa_status pa_block_decref(pa_allocator* a, int32_t block);
+int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
+int32_t pa_num_free_blocks(const pa_allocator* a);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

@@ -1,0 +1,281 @@
+"""Paged attention forward for MI355X: Python binding of libpa.so.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libpa.so; PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing, importing this package
+raises.
+
+The function names follow the C ABI in include/pa.h:
+  write_kv, gather_kv, prefill, decode, decode_num_splits,
+  decode_workspace_bytes, write_kv_workspace_bytes, BlockAllocator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_OOM, PA_ERR_LAUNCH = \
+    0, -1, -2, -3, -4, -5
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m online_softmax_paged_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int)]
+
+
+_P, _I32, _F, _SZ, _VP = ctypes.POINTER(_Pool), ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype, f.argtypes = res, args
+    return f
+
+
+_status_string = _sig("pa_status_string", ctypes.c_char_p, [ctypes.c_int])
+_abi_version = _sig("pa_abi_version", _I32, [])
+_write_ws = _sig("pa_write_kv_workspace_bytes", _SZ, [_P])
+_write = _sig("pa_write_kv", ctypes.c_int, [_P, _VP, _VP, ctypes.c_int, _VP, _I32, _VP, _SZ, _VP])
+_gather = _sig("pa_gather_kv", ctypes.c_int, [_P, _VP, _I32, _VP, _VP, _I32, _I32, _VP, _VP, _VP])
+_prefill = _sig("pa_prefill", ctypes.c_int,
+                [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                 _F, _I32, _VP])
+_num_splits = _sig("pa_decode_num_splits", _I32, [_I32, _I32, _I32])
+_dec_ws = _sig("pa_decode_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
+_decode = _sig("pa_decode", ctypes.c_int,
+               [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F, _I32,
+                _VP, _SZ, _VP])
+_alloc_create = _sig("pa_allocator_create", _VP, [_I32])
+_alloc_destroy = _sig("pa_allocator_destroy", None, [_VP])
+_alloc_block = _sig("pa_alloc_block", _I32, [_VP])
+_incref = _sig("pa_block_incref", ctypes.c_int, [_VP, _I32])
+_decref = _sig("pa_block_decref", ctypes.c_int, [_VP, _I32])
+_refcount = _sig("pa_block_refcount", _I32, [_VP, _I32])
+_num_free = _sig("pa_num_free_blocks", _I32, [_VP])
+
+EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes", "pa_write_kv",
+            "pa_gather_kv", "pa_prefill", "pa_decode_num_splits", "pa_decode_workspace_bytes",
+            "pa_decode", "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_block",
+            "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks"]
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def status_string(s: int) -> str:
+    return _status_string(s).decode()
+
+
+def abi_version() -> int:
+    return int(_abi_version())
+
+
+def _check(status: int, what: str):
+    if status != PA_OK:
+        raise PAError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}
+_NAMES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+class KVPool:
+    """Device tensors of one KV block pool (layout in include/pa.h):
+    k [NB, Hkv, 16, D], v [NB, Hkv, D, 16]; fp8 pools are uint8 codes plus
+    float32 k_scale / v_scale [NB]."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str,
+                 device="cuda", fill_nan: bool = True):
+        dt = _NAMES[kv_dtype]
+        self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
+        self.kv_dtype = kv_dtype
+        nan = {"f32": float("nan"), "bf16": float("nan"), "fp8": 0x7F}[kv_dtype]
+        shape_k = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
+        shape_v = (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE)
+        if fill_nan:
+            self.k = torch.full(shape_k, nan, dtype=dt, device=device)
+            self.v = torch.full(shape_v, nan, dtype=dt, device=device)
+        else:
+            self.k = torch.empty(shape_k, dtype=dt, device=device)
+            self.v = torch.empty(shape_v, dtype=dt, device=device)
+        if kv_dtype == "fp8":
+            self.k_scale = torch.full((num_blocks,), float("nan"), dtype=torch.float32, device=device)
+            self.v_scale = torch.full((num_blocks,), float("nan"), dtype=torch.float32, device=device)
+        else:
+            self.k_scale = self.v_scale = None
+        self._c = _Pool(self.k.data_ptr(), self.v.data_ptr(),
+                        self.k_scale.data_ptr() if self.k_scale is not None else None,
+                        self.v_scale.data_ptr() if self.v_scale is not None else None,
+                        num_blocks, num_kv_heads, head_dim, BLOCK_SIZE, _DT[dt])
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+    def nbytes(self) -> int:
+        n = self.k.numel() * self.k.element_size() * 2
+        if self.k_scale is not None:
+            n += 2 * self.k_scale.numel() * 4
+        return n
+
+
+def write_kv_workspace_bytes(pool: KVPool) -> int:
+    return int(_write_ws(pool.c))
+
+
+def write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+             workspace: torch.Tensor | None = None, stream=None):
+    """Scatter (and for fp8 pools, quantise per block) new tokens into the pool."""
+    n = int(slot_mapping.numel())
+    need = write_kv_workspace_bytes(pool)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_new.device)
+    _check(_write(pool.c, _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], _ptr(slot_mapping), n,
+                  _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                  _stream(stream)), "pa_write_kv")
+
+
+def gather_kv(pool: KVPool, block_table, ctx_lens, max_ctx_len: int, stream=None):
+    """Copy each sequence's tokens out of the pool -> (k, v) [sum ctx, Hkv, D]."""
+    B = int(ctx_lens.numel())
+    cu = torch.zeros(B + 1, dtype=torch.int32, device=ctx_lens.device)
+    cu[1:] = torch.cumsum(ctx_lens, 0)
+    total = int(cu[-1].item())
+    shape = (total, pool.num_kv_heads, pool.head_dim)
+    k_out = torch.empty(shape, dtype=pool.k.dtype, device=pool.k.device)
+    v_out = torch.empty(shape, dtype=pool.k.dtype, device=pool.k.device)
+    _check(_gather(pool.c, _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), _ptr(cu), B,
+                   max_ctx_len, _ptr(k_out), _ptr(v_out), _stream(stream)), "pa_gather_kv")
+    return k_out, v_out
+
+
+def _validate(pool: KVPool, ctx_lens, block_table, q_lens=None):
+    """Host-side check of the device-resident metadata contract (copies to CPU)."""
+    ctx = ctx_lens.cpu().tolist()
+    bt = block_table.cpu()
+    for b, c in enumerate(ctx):
+        if c < 1:
+            raise ValueError(f"sequence {b}: ctx_len {c} < 1")
+        n = (c + BLOCK_SIZE - 1) // BLOCK_SIZE
+        if n > bt.shape[1]:
+            raise ValueError(f"sequence {b}: block table too short")
+        ids = bt[b, :n]
+        if (ids < 0).any() or (ids >= pool.num_blocks).any():
+            raise ValueError(f"sequence {b}: block id out of range")
+        if q_lens is not None and not (1 <= q_lens[b] <= c):
+            raise ValueError(f"sequence {b}: q_len {q_lens[b]} not in [1, {c}]")
+
+
+def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, scale: float,
+            causal: bool = True, max_q_len: int | None = None, max_ctx_len: int | None = None,
+            out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+            validate: bool = False, stream=None):
+    """Attention of query chunks (the last q_len_b positions of each sequence).
+    Returns (o, lse): o like q, lse float32 [T, Hq]."""
+    B = int(ctx_lens.numel())
+    if max_q_len is None or max_ctx_len is None or validate:
+        cu = cu_q_lens.cpu()
+        q_lens = (cu[1:] - cu[:-1]).tolist()
+        if max_q_len is None:
+            max_q_len = max(q_lens) if q_lens else 0
+        if max_ctx_len is None:
+            max_ctx_len = int(ctx_lens.max().item()) if B else 0
+        if validate:
+            _validate(pool, ctx_lens, block_table, q_lens)
+    T, Hq, _ = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _check(_prefill(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(cu_q_lens),
+                    _ptr(ctx_lens), _ptr(block_table), block_table.shape[1], B, Hq, max_q_len,
+                    max_ctx_len, scale, 1 if causal else 0, _stream(stream)), "pa_prefill")
+    return o, lse
+
+
+def decode_num_splits(num_seqs: int, num_kv_heads: int, max_ctx_len: int) -> int:
+    return int(_num_splits(num_seqs, num_kv_heads, max_ctx_len))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(_dec_ws(num_seqs, num_q_heads, head_dim, num_splits))
+
+
+def decode(pool: KVPool, q: torch.Tensor, ctx_lens, block_table, scale: float,
+           max_ctx_len: int | None = None, num_splits: int = 0,
+           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, validate: bool = False, stream=None):
+    """One query per sequence at its last position.  Returns (o, lse)."""
+    B, Hq, D = q.shape
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_lens.max().item())
+    if validate:
+        _validate(pool, ctx_lens, block_table)
+    if num_splits == 0:
+        num_splits = decode_num_splits(B, pool.num_kv_heads, max_ctx_len)
+    need = decode_workspace_bytes(B, Hq, D, num_splits)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(_decode(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(ctx_lens),
+                   _ptr(block_table), block_table.shape[1], B, Hq, max_ctx_len, scale,
+                   num_splits, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                   _stream(stream)), "pa_decode")
+    return o, lse
+
+
+class BlockAllocator:
+    """Host block allocator of the library (free list + reference counts)."""
+
+    def __init__(self, num_blocks: int):
+        self._h = _alloc_create(num_blocks)
+        if not self._h:
+            raise ValueError("pa_allocator_create failed")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            _alloc_destroy(h)
+
+    def alloc(self) -> int:
+        return int(_alloc_block(self._h))
+
+    def incref(self, block: int):
+        _check(_incref(self._h, block), "pa_block_incref")
+
+    def decref(self, block: int):
+        _check(_decref(self._h, block), "pa_block_decref")
+
+    def refcount(self, block: int) -> int:
+        return int(_refcount(self._h, block))
+
+    def num_free(self) -> int:
+        return int(_num_free(self._h))

@@ -1,0 +1,203 @@
+// C ABI of libpa: host-side argument checks, then dispatch to the launchers.
+// Every check runs before anything is enqueued; no HIP call happens on a
+// failed check.
+#include <math.h>
+
+#include "pa_internal.h"
+
+using namespace pa;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_pool(const pa_kv_pool* pool) {
+  if (!pool || !pool->k || !pool->v) return PA_ERR_INVALID_ARG;
+  if (pool->block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (pool->num_blocks < 1 || pool->num_kv_heads < 1) return PA_ERR_INVALID_ARG;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (pool->kv_dtype != PA_F32 && pool->kv_dtype != PA_BF16 && pool->kv_dtype != PA_FP8_E4M3)
+    return PA_ERR_INVALID_ARG;
+  if (pool->kv_dtype == PA_FP8_E4M3 && (!pool->k_scale || !pool->v_scale))
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(pool->k) || !aligned16(pool->v)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+pa_status check_attn(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, const void* o,
+                     const int32_t* ctx_lens, const int32_t* block_table, int32_t bt_stride,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx_len, float scale) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  if (num_seqs < 0) return PA_ERR_INVALID_ARG;
+  if (!q || !o || !ctx_lens || !block_table) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o)) return PA_ERR_INVALID_ARG;
+  if (q_dtype == PA_F32) {
+    if (pool->kv_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  } else if (q_dtype == PA_BF16) {
+    if (pool->kv_dtype != PA_BF16 && pool->kv_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  } else {
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  int g = num_q_heads / pool->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return PA_ERR_UNSUPPORTED;
+  if (max_ctx_len < 1) return PA_ERR_INVALID_ARG;
+  if (bt_stride < (max_ctx_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+AttnArgs make_args(const pa_kv_pool* pool, const void* q, void* o, float* lse,
+                   const int32_t* ctx_lens, const int32_t* block_table, int32_t bt_stride,
+                   int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx_len, float scale) {
+  AttnArgs a{};
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.kv_dtype = pool->kv_dtype;
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.ctx_lens = ctx_lens;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_ctx_len = max_ctx_len;
+  a.scale = scale;
+  return a;
+}
+
+pa_status launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, group size or block size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_OOM: return "no free block";
+    case PA_ERR_LAUNCH: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t pa_abi_version(void) { return 1; }
+
+size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
+  if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
+  return 2 * sizeof(uint32_t) * static_cast<size_t>(pool->num_blocks);
+}
+
+pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_INVALID_ARG;
+  if (pool->kv_dtype == PA_FP8_E4M3) {
+    if (src_dtype != PA_F32 && src_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < pa_write_kv_workspace_bytes(pool)) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  } else if (src_dtype != pool->kv_dtype) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  return launched(launch_write_kv(*pool, k_new, v_new, src_dtype, slot_mapping, num_tokens,
+                                  static_cast<uint32_t*>(workspace),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* ctx_lens, const int32_t* cu_ctx, int32_t num_seqs,
+                       int32_t max_ctx_len, void* k_out, void* v_out, void* stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  if (num_seqs < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!block_table || !ctx_lens || !cu_ctx || !k_out || !v_out) return PA_ERR_INVALID_ARG;
+  if (max_ctx_len < 1 || bt_stride < (max_ctx_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE)
+    return PA_ERR_INVALID_ARG;
+  return launched(launch_gather_kv(*pool, block_table, bt_stride, ctx_lens, cu_ctx, num_seqs,
+                                   max_ctx_len, k_out, v_out, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                     float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                     const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                     float scale, int32_t causal, void* stream) {
+  if (num_seqs == 0 && pool) return check_pool(pool);
+  pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
+                           num_q_heads, max_ctx_len, scale);
+  if (s != PA_OK) return s;
+  if (!cu_q_lens || max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
+  AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
+                         num_q_heads, max_ctx_len, scale);
+  a.cu_q_lens = cu_q_lens;
+  a.max_q_len = max_q_len;
+  a.causal = causal ? 1 : 0;
+  return launched(launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len) {
+  if (num_seqs < 1 || num_kv_heads < 1 || max_ctx_len < 1) return 1;
+  const int32_t pages = (max_ctx_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+  // Aim for about 1024 workgroups (4 per compute unit) while keeping at least
+  // 8 pages (2 per wave) in every split.
+  const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  int64_t s = (1024 + base - 1) / base;
+  int64_t max_by_pages = pages / 8;
+  if (s > max_by_pages) s = max_by_pages;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return static_cast<int32_t>(s);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t num_splits) {
+  if (num_seqs < 1 || num_q_heads < 1 || head_dim < 1 || num_splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * num_splits;
+  size_t o_bytes = rows * head_dim * sizeof(float);
+  o_bytes = (o_bytes + 255) & ~static_cast<size_t>(255);
+  return o_bytes + rows * sizeof(float);
+}
+
+pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                    float* lse, const int32_t* ctx_lens, const int32_t* block_table,
+                    int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_ctx_len, float scale, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (num_seqs == 0 && pool) return check_pool(pool);
+  pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
+                           num_q_heads, max_ctx_len, scale);
+  if (s != PA_OK) return s;
+  if (num_splits < 0 || num_splits > 256) return PA_ERR_INVALID_ARG;
+  if (num_splits == 0) num_splits = pa_decode_num_splits(num_seqs, pool->num_kv_heads, max_ctx_len);
+  AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
+                         num_q_heads, max_ctx_len, scale);
+  a.num_splits = num_splits;
+  if (num_splits > 1) {
+    size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim, num_splits);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+    size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * num_splits;
+    size_t o_bytes = (rows * pool->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  }
+  return launched(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,362 @@
+// Split-KV decode: one query token per sequence against its paged K/V.
+//
+// Pass 1 (split kernel): workgroup = (page range s, KV head g, sequence b),
+// four waves.  Each wave walks every fourth page of the range; per 16-token
+// page it reads the K page and the V page straight from HBM into MFMA operand
+// registers (16-byte / 8-byte loads), computes the scores of all the group's
+// query heads at once on the matrix cores, and folds them into a running max,
+// running sum and rescaled accumulator (the online softmax of the "core
+// modules" chapter, section 2.1; deferred division as in FlashAttention-2).
+// The four waves then combine through LDS and write one normalised partial
+// output and logsumexp per query head (or the final result when there is a
+// single range).
+//
+// Pass 2 (merge kernel): per (sequence, query head), combine the ranges by
+// their logsumexps.
+//
+// Operand layouts (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16,
+// lane l, c = l % 16, grp = l / 16):
+//   scores S^T = K . Q^T : A = K rows (key c), B = Q^T columns (head c);
+//                          D[4*grp + i][c] = score of key 4*grp+i, head c
+//   O^T += V^T . P^T     : A = V^T rows (feature c), B = P^T (the lane's own
+//                          4 scores, head c); D[4*grp + i][c] = O[head c][feat]
+// so each lane keeps the softmax state of head c and no transpose is needed.
+// Scores are kept in the log2 domain (scale * log2(e) folded in) and
+// exponentiated with the hardware exp2.
+#include <float.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int D>
+struct KVFrag {
+  bf16x8 k[D / 32];  // A operand of the score MFMA, one per 32-feature step
+  bf16x4 v[D / 16];  // A operand of the PV MFMA, one per 16-feature block
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_page(KVFrag<D>& f, const void* kbase, const void* vbase,
+                                          int64_t chunk, int lane) {
+  const int c = lane & 15, grp = lane >> 4;
+  if constexpr (!FP8) {
+    const uint16_t* kp = static_cast<const uint16_t*>(kbase) + chunk * (kPage * D);
+    const uint16_t* vp = static_cast<const uint16_t*>(vbase) + chunk * (kPage * D);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      f.k[ks] = *reinterpret_cast<const bf16x8*>(kp + c * D + ks * 32 + grp * 8);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      f.v[db] = *reinterpret_cast<const bf16x4*>(vp + (db * 16 + c) * kPage + grp * 4);
+  } else {
+    const uint8_t* kp = static_cast<const uint8_t*>(kbase) + chunk * (kPage * D);
+    const uint8_t* vp = static_cast<const uint8_t*>(vbase) + chunk * (kPage * D);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(kp + c * D + ks * 32 + grp * 8);
+      const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
+      u32x4 r;
+      r.x = lo.x; r.y = lo.y; r.z = hi.x; r.w = hi.y;
+      f.k[ks] = __builtin_bit_cast(bf16x8, r);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + (db * 16 + c) * kPage + grp * 4);
+      f.v[db] = __builtin_bit_cast(bf16x4, fp8x4_to_bf16x4(w));
+    }
+  }
+}
+
+__device__ __forceinline__ bool valid_block(int32_t phys, int32_t nb) {
+  return phys >= 0 && phys < nb;
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void decode_split_kernel(AttnArgs a) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 15, grp = lane >> 4;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int S = a.num_splits;
+
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  const int n_pages = (ctx + kPage - 1) / kPage;
+  const int max_pages = (a.max_ctx_len + kPage - 1) / kPage;
+  const int pps = (max_pages + S - 1) / S;
+  const int p_begin = split * pps;
+  const int p_end = min(p_begin + pps, n_pages);
+
+  // Q^T operand: column c = query head g*G + c (zero for c >= G).
+  bf16x8 qf[D / 32];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(b) * Hq + g * G + (c < G ? c : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + grp * 8);
+      if (c >= G) v = bf16x8{};
+      qf[ks] = v;
+    }
+  }
+  const float sc = a.scale * kLog2e;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  KVFrag<D> cur, nxt;
+  int p = p_begin + wave;
+  int32_t phys = p < p_end ? bt[p] : -1;
+  if (p < p_end && valid_block(phys, a.num_blocks))
+    load_page<D, FP8>(cur, a.k, a.v, static_cast<int64_t>(phys) * Hkv + g, lane);
+
+  for (; p < p_end; p += kWaves) {
+    const int pn = p + kWaves;
+    const int32_t phys_n = pn < p_end ? bt[pn] : -1;
+    if (pn < p_end && valid_block(phys_n, a.num_blocks))
+      load_page<D, FP8>(nxt, a.k, a.v, static_cast<int64_t>(phys_n) * Hkv + g, lane);
+
+    if (valid_block(phys, a.num_blocks)) {
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[ks], qf[ks], s4, 0, 0, 0);
+      float scl = sc, vscl = 1.f;
+      if constexpr (FP8) {
+        scl *= a.k_scale[phys];
+        vscl = a.v_scale[phys];
+      }
+      const int key0 = p * kPage + grp * 4;
+      float s[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (key0 + i < ctx) ? s4[i] * scl : -INFINITY;
+      float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - m_new);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
+      l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      m = m_new;
+      u32x2 pp;
+      pp.x = pack_bf16x2(pr[0] * vscl, pr[1] * vscl);
+      pp.y = pack_bf16x2(pr[2] * vscl, pr[3] * vscl);
+      const bf16x4 pf = __builtin_bit_cast(bf16x4, pp);
+      if (p * kPage + kPage > ctx) {
+        // Last, partly filled page: slots past the context hold unspecified
+        // bytes (possibly NaN); replace them so that 0 * NaN cannot occur.
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          u32x2 w = __builtin_bit_cast(u32x2, cur.v[db]);
+          if (key0 + 0 >= ctx) w.x &= 0xffff0000u;
+          if (key0 + 1 >= ctx) w.x &= 0x0000ffffu;
+          if (key0 + 2 >= ctx) w.y &= 0xffff0000u;
+          if (key0 + 3 >= ctx) w.y &= 0x0000ffffu;
+          cur.v[db] = __builtin_bit_cast(bf16x4, w);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        acc[db] *= alpha;
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(i16x4, cur.v[db]), __builtin_bit_cast(i16x4, pf), acc[db], 0,
+            0, 0);
+      }
+    }
+    cur = nxt;
+    phys = phys_n;
+  }
+
+  // Row sums: each lane group holds a quarter of the keys of head c.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
+  __shared__ float sm_o[kWaves][D][17];
+  if (grp == 0) {
+    sm_m[wave][c] = m;
+    sm_l[wave][c] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[wave][db * 16 + grp * 4 + i][c] = acc[db][i];
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int hd = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][hd]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][hd];
+        if (mw != -INFINITY) {
+          const float f = fast_exp2(mw - M);
+          L += sm_l[w][hd] * f;
+          O += sm_o[w][d][hd] * f;
+        }
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float out = empty ? 0.f : O / L;
+    const float lse = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
+    const int64_t row = static_cast<int64_t>(b) * Hq + g * G + hd;
+    if (S == 1) {
+      static_cast<uint16_t*>(a.o)[row * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(out));
+      if (d == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      a.ws_o[(row * S + split) * D + d] = out;
+      if (d == 0) a.ws_lse[row * S + split] = lse;
+    }
+  }
+}
+
+// fp32 pools: one wave per (query head, sequence, page range); lane owns
+// features lane and lane + 64.  Plain FMA arithmetic with wave reductions.
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * kWaves + wave;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, S = a.num_splits;
+  if (h >= Hq) return;
+  const int g = h / G;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  const int max_pages = (a.max_ctx_len + kPage - 1) / kPage;
+  const int pps = (max_pages + S - 1) / S;
+  const int t_begin = split * pps * kPage;
+  const int t_end = min(t_begin + pps * kPage, ctx);
+  constexpr int NPL = D / 64;  // features per lane
+  const float* qp = static_cast<const float*>(a.q) + (static_cast<int64_t>(b) * Hq + h) * D;
+  float q[NPL], o[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    q[j] = qp[lane + 64 * j];
+    o[j] = 0.f;
+  }
+  const float* kb = static_cast<const float*>(a.k);
+  const float* vb = static_cast<const float*>(a.v);
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const float sc = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  for (int t = t_begin; t < t_end; ++t) {
+    const int32_t phys = bt[t / kPage];
+    if (!valid_block(phys, a.num_blocks)) continue;
+    const int64_t chunk = (static_cast<int64_t>(phys) * Hkv + g) * kPage * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) dot += q[j] * kb[chunk + (t % kPage) * D + lane + 64 * j];
+    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s);
+    const float s2 = dot * sc;
+    const float m_new = fmaxf(m, s2);
+    const float alpha = fast_exp2(m - m_new);
+    const float pr = fast_exp2(s2 - m_new);
+    l = l * alpha + pr;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      o[j] = o[j] * alpha + pr * vb[chunk + (lane + 64 * j) * kPage + t % kPage];
+    m = m_new;
+  }
+  const bool empty = !(l > 0.f);
+  const float lse = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+  const int64_t row = static_cast<int64_t>(b) * Hq + h;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const float out = empty ? 0.f : o[j] / l;
+    if (S == 1)
+      static_cast<float*>(a.o)[row * D + lane + 64 * j] = out;
+    else
+      a.ws_o[(row * S + split) * D + lane + 64 * j] = out;
+  }
+  if (lane == 0) {
+    if (S == 1) {
+      if (a.lse) a.lse[row] = lse;
+    } else {
+      a.ws_lse[row * S + split] = lse;
+    }
+  }
+}
+
+// One wave per (sequence, query head): logsumexp-weighted sum of the ranges.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  if (row >= rows) return;
+  const int S = a.num_splits;
+  const float* ls = a.ws_lse + row * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ls[s]);
+  constexpr int NPL = D / 64;
+  float o[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) o[j] = 0.f;
+  float W = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float lsv = ls[s];
+      if (lsv == -INFINITY) continue;
+      const float w = fast_exp2((lsv - M) * kLog2e);
+      W += w;
+      const float* op = a.ws_o + (row * S + s) * D;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) o[j] += w * op[lane + 64 * j];
+    }
+  }
+  const bool empty = !(W > 0.f);
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const float out = empty ? 0.f : o[j] / W;
+    if constexpr (sizeof(OutT) == 2)
+      static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] =
+          static_cast<uint16_t>(f32_to_bf16_bits(out));
+    else
+      static_cast<float*>(a.o)[row * D + lane + 64 * j] = out;
+  }
+  if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : M + __logf(W);
+}
+
+template <int D>
+hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
+  const int S = a.num_splits;
+  if (a.kv_dtype == PA_F32) {
+    const dim3 grid(S, (a.num_q_heads + kWaves - 1) / kWaves, a.num_seqs);
+    decode_f32_kernel<D><<<grid, 256, 0, st>>>(a);
+  } else {
+    const dim3 grid(S, a.num_kv_heads, a.num_seqs);
+    if (a.kv_dtype == PA_FP8_E4M3)
+      decode_split_kernel<D, true><<<grid, 256, 0, st>>>(a);
+    else
+      decode_split_kernel<D, false><<<grid, 256, 0, st>>>(a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  const unsigned blocks = static_cast<unsigned>((rows + kWaves - 1) / kWaves);
+  if (a.kv_dtype == PA_F32)
+    decode_merge_kernel<D, float><<<blocks, 256, 0, st>>>(a);
+  else
+    decode_merge_kernel<D, uint16_t><<<blocks, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const AttnArgs& a, hipStream_t st) {
+  return a.head_dim == 64 ? launch_decode_d<64>(a, st) : launch_decode_d<128>(a, st);
+}
+
+}  // namespace pa

@@ -1,0 +1,104 @@
+// Internal declarations shared by the HIP sources of libpa (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kPage = 16;          // tokens per physical block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats -> two bf16 packed in one dword (low = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// fp8 E4M3 (OCP) byte -> float, via the hardware converter.
+__device__ __forceinline__ float fp8_to_f32(uint32_t word, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(word, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(word, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(word, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(word, 3);
+  }
+}
+
+// Four fp8 codes in a dword -> four bf16 packed in two dwords (exact: every
+// E4M3 value is a bfloat16 value).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  float f0 = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+  float f1 = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+  float f2 = __builtin_amdgcn_cvt_f32_fp8(w, 2);
+  float f3 = __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  u32x2 r;
+  r.x = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  r.y = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already checked.
+hipError_t launch_write_kv(const pa_kv_pool& pool, const void* k_new, const void* v_new,
+                           pa_dtype src, const int32_t* slots, int32_t n, uint32_t* amax_ws,
+                           hipStream_t st);
+hipError_t launch_gather_kv(const pa_kv_pool& pool, const int32_t* bt, int32_t bt_stride,
+                            const int32_t* ctx, const int32_t* cu_ctx, int32_t B,
+                            int32_t max_ctx, void* k_out, void* v_out, hipStream_t st);
+
+struct AttnArgs {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pa_dtype kv_dtype;
+  const void* q;
+  void* o;
+  float* lse;
+  const int32_t* cu_q_lens;   // prefill only
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t max_q_len;
+  int32_t max_ctx_len;
+  float scale;
+  int32_t causal;
+  int32_t num_splits;          // decode only
+  float* ws_o;                 // decode: [B, Hq, S, D] partial outputs
+  float* ws_lse;               // decode: [B, Hq, S] partial logsumexp
+};
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t st);
+hipError_t launch_decode(const AttnArgs& a, hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,402 @@
+// Causal (or full) prefill over the paged KV cache.
+//
+// FlashAttention-style tiling (survey page, section 2, core principle: Q in
+// row blocks, K/V in column blocks, one block at a time on chip, combined
+// through running max and exp-sum statistics; FlashAttention-2's deferred
+// division and parallelism over the sequence).  Here:
+//
+//  * Workgroup = 4 waves = 128 query rows of one KV head group: 128/G query
+//    tokens times the G query heads that share KV head g (grouped-query
+//    packing, so every K/V tile read from HBM serves all G heads).
+//  * K/V tiles of 32 keys = two 16-token physical pages, found through the
+//    block table, staged in LDS (double-buffered: the next tile's global loads
+//    are in flight while the current one is multiplied).
+//  * Per wave, v_mfma_f32_32x32x16_bf16 computes S^T = K . Q^T (keys x 32
+//    queries; Q^T stays in registers for the whole kernel) so that each lane
+//    owns one query column: its softmax state (m, l) and its column of
+//    O^T = V^T . P^T need no cross-lane traffic except one swap with lane^32.
+//  * fp8 pools are expanded to bf16 on the way into LDS (exact); the page's K
+//    scale multiplies the score columns and its V scale the probabilities.
+//  * Grid = (sequence x KV head, query tile) with tiles launched longest
+//    first, so the long diagonal tiles start early and each (sequence, KV
+//    head)'s tiles spread over all dies while their K/V stays L2-resident.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kRows = 128;   // query rows per workgroup
+constexpr int kKeys = 32;    // keys per tile (2 pages)
+
+template <int D>
+struct Smem {
+  static constexpr int KS = D + 8;        // K row stride (bf16), 16 B pad
+  static constexpr int VS = kKeys + 4;    // V^T row stride (bf16), 8 B pad
+  uint16_t k[2][kKeys * KS];
+  uint16_t vt[2][D * VS];
+};
+
+// Global -> register staging of one 32-key tile.
+template <int D, bool FP8>
+struct Stage {
+  // bf16: K 2 chunks of 16 B, V 2 chunks of 16 B per thread (D=128).
+  // fp8:  K 1 chunk, V 1 chunk per thread (16 fp8 = 16 B).
+  static constexpr int KCH = FP8 ? (kKeys * D / 16 + 255) / 256 : (kKeys * D / 8 + 255) / 256;
+  static constexpr int VCH = KCH;
+  u32x4 k[KCH];
+  u32x4 v[VCH];
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const AttnArgs& a, int g,
+                                           const int32_t* bt, int kt, int ctx, int tid) {
+  const int Hkv = a.num_kv_heads;
+  if constexpr (!FP8) {
+    constexpr int CPP = kPage * D / 8;  // 16-byte chunks per page
+#pragma unroll
+    for (int r = 0; r < st.KCH; ++r) {
+      const int e = r * 256 + tid;
+      const int pg = e / CPP, within = e % CPP;
+      const int tok = kt * kKeys + pg * kPage;
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (e < 2 * CPP && tok < ctx) {
+        const int32_t phys = bt[tok / kPage];
+        if (phys >= 0 && phys < a.num_blocks) {
+          const int64_t base = (static_cast<int64_t>(phys) * Hkv + g) * (kPage * D);
+          kv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + base + within * 8);
+          vv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + base + within * 8);
+        }
+      }
+      st.k[r] = kv;
+      st.v[r] = vv;
+    }
+  } else {
+    constexpr int CPP = kPage * D / 16;
+#pragma unroll
+    for (int r = 0; r < st.KCH; ++r) {
+      const int e = r * 256 + tid;
+      const int pg = e / CPP, within = e % CPP;
+      const int tok = kt * kKeys + pg * kPage;
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (e < 2 * CPP && tok < ctx) {
+        const int32_t phys = bt[tok / kPage];
+        if (phys >= 0 && phys < a.num_blocks) {
+          const int64_t base = (static_cast<int64_t>(phys) * Hkv + g) * (kPage * D);
+          kv = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k) + base + within * 16);
+          vv = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) + base + within * 16);
+        }
+      }
+      st.k[r] = kv;
+      st.v[r] = vv;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t zero_lo_hi(uint32_t w, bool lo_dead, bool hi_dead) {
+  if (lo_dead) w &= 0xffff0000u;
+  if (hi_dead) w &= 0x0000ffffu;
+  return w;
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm, int buf, int kt,
+                                            int ctx, int tid) {
+  constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
+  if constexpr (!FP8) {
+    constexpr int CPP = kPage * D / 8;
+#pragma unroll
+    for (int r = 0; r < st.KCH; ++r) {
+      const int e = r * 256 + tid;
+      if (e >= 2 * CPP) break;
+      const int pg = e / CPP, within = e % CPP;
+      // K chunk: token within / (D/8), features (within % (D/8)) * 8
+      const int tk = within / (D / 8), dc = within % (D / 8);
+      const int key = pg * kPage + tk;
+      u32x4 kv = st.k[r];
+      if (kt * kKeys + key >= ctx) kv = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(&sm.k[buf][key * KS + dc * 8]) = kv;
+      // V^T chunk: feature within / 2, tokens (within % 2) * 8 .. + 8
+      const int d = within >> 1, half = within & 1;
+      const int t0 = kt * kKeys + pg * kPage + half * 8;
+      u32x4 vv = st.v[r];
+      if (t0 + 8 > ctx) {
+        vv.x = zero_lo_hi(vv.x, t0 + 0 >= ctx, t0 + 1 >= ctx);
+        vv.y = zero_lo_hi(vv.y, t0 + 2 >= ctx, t0 + 3 >= ctx);
+        vv.z = zero_lo_hi(vv.z, t0 + 4 >= ctx, t0 + 5 >= ctx);
+        vv.w = zero_lo_hi(vv.w, t0 + 6 >= ctx, t0 + 7 >= ctx);
+      }
+      uint16_t* dst = &sm.vt[buf][d * VS + pg * kPage + half * 8];
+      *reinterpret_cast<u32x2*>(dst) = u32x2{vv.x, vv.y};
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{vv.z, vv.w};
+    }
+  } else {
+    constexpr int CPP = kPage * D / 16;
+#pragma unroll
+    for (int r = 0; r < st.KCH; ++r) {
+      const int e = r * 256 + tid;
+      if (e >= 2 * CPP) break;
+      const int pg = e / CPP, within = e % CPP;
+      // K chunk: 16 features of one token
+      const int tk = within / (D / 16), dc = within % (D / 16);
+      const int key = pg * kPage + tk;
+      const u32x4 kw = st.k[r];
+      u32x2 k0 = fp8x4_to_bf16x4(kw.x), k1 = fp8x4_to_bf16x4(kw.y);
+      u32x2 k2 = fp8x4_to_bf16x4(kw.z), k3 = fp8x4_to_bf16x4(kw.w);
+      u32x4 ka = {k0.x, k0.y, k1.x, k1.y}, kb = {k2.x, k2.y, k3.x, k3.y};
+      if (kt * kKeys + key >= ctx) ka = kb = u32x4{0, 0, 0, 0};
+      uint16_t* kd = &sm.k[buf][key * KS + dc * 16];
+      *reinterpret_cast<u32x4*>(kd) = ka;
+      *reinterpret_cast<u32x4*>(kd + 8) = kb;
+      // V^T chunk: all 16 tokens of one feature row
+      const int d = within;
+      const int t0 = kt * kKeys + pg * kPage;
+      const u32x4 vw = st.v[r];
+      u32x2 w[4] = {fp8x4_to_bf16x4(vw.x), fp8x4_to_bf16x4(vw.y), fp8x4_to_bf16x4(vw.z),
+                    fp8x4_to_bf16x4(vw.w)};
+      if (t0 + kPage > ctx) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[j].x = zero_lo_hi(w[j].x, t0 + 4 * j + 0 >= ctx, t0 + 4 * j + 1 >= ctx);
+          w[j].y = zero_lo_hi(w[j].y, t0 + 4 * j + 2 >= ctx, t0 + 4 * j + 3 >= ctx);
+        }
+      }
+      uint16_t* vd = &sm.vt[buf][d * VS + pg * kPage];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(vd + 4 * j) = w[j];
+    }
+  }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
+  __shared__ Smem<D> sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y);
+  const int TQ = kRows / G;
+
+  const int q0 = a.cu_q_lens[b];
+  const int qlen = a.cu_q_lens[b + 1] - q0;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  const int t0 = tile * TQ;
+  if (t0 >= qlen) return;
+  const int pos_base = ctx - qlen;            // position of query token 0
+  const int t_last = min(t0 + TQ, qlen) - 1;  // last token of this tile
+  const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
+  if (kmax <= 0) return;                      // inconsistent lengths: nothing visible
+  const int n_kt = (kmax + kKeys - 1) / kKeys;
+  // Tiles whose keys are all visible to every row need no mask.
+  const int first_pos = pos_base + t0;
+  const int n_full = a.causal ? max(0, min((first_pos + 1) / kKeys, ctx / kKeys))
+                              : ctx / kKeys;
+
+  // This lane's query row.
+  const int r = wave * 32 + col;
+  const int tt = t0 + r / G, hg = r % G;
+  const bool row_ok = tt < qlen;
+  const int qpos = pos_base + tt;
+  const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
+
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
+  }
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const float sc = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  Stage<D, FP8> st;
+  stage_load<D, FP8>(st, a, g, bt, 0, ctx, tid);
+  stage_store<D, FP8>(st, sm, 0, 0, ctx, tid);
+  __syncthreads();
+
+  constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) stage_load<D, FP8>(st, a, g, bt, kt + 1, ctx, tid);
+
+    // S^T = K . Q^T  (32 keys x 32 queries)
+    f32x16 s = {};
+    const uint16_t* kb = &sm.k[buf][col * KS + half * 8];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+    float sc0 = sc, sc1 = sc, vs0 = 1.f, vs1 = 1.f;
+    if constexpr (FP8) {
+      const int tok = kt * kKeys;
+      const int32_t p0 = bt[tok / kPage];
+      const bool has1 = tok + kPage < ctx;
+      const int32_t p1 = has1 ? bt[tok / kPage + 1] : -1;
+      const bool ok0 = p0 >= 0 && p0 < a.num_blocks, ok1 = p1 >= 0 && p1 < a.num_blocks;
+      sc0 *= ok0 ? a.k_scale[p0] : 0.f;
+      vs0 = ok0 ? a.v_scale[p0] : 0.f;
+      sc1 *= ok1 ? a.k_scale[p1] : 0.f;
+      vs1 = ok1 ? a.v_scale[p1] : 0.f;
+    }
+    // Score value i of this lane is key 8*(i/4) + 4*half + i%4 of the tile.
+    float sv[16];
+    const bool masked = kt >= n_full;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kt * kKeys + 8 * (i >> 2) + 4 * half + (i & 3);
+      float x = s[i] * (i < 8 ? sc0 : sc1);
+      if (masked) {
+        const bool vis = key < ctx && (!a.causal || key <= qpos);
+        x = vis ? x : -INFINITY;
+      }
+      sv[i] = x;
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = fast_exp2(sv[i] - m_use);
+      psum += sv[i];
+    }
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+
+    // O^T += V^T . P^T ; chunk c covers page c of the tile (keys 16c..16c+15)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float vsc = c == 0 ? vs0 : vs1;
+      u32x4 pw;
+      pw.x = pack_bf16x2(sv[8 * c + 0] * vsc, sv[8 * c + 1] * vsc);
+      pw.y = pack_bf16x2(sv[8 * c + 2] * vsc, sv[8 * c + 3] * vsc);
+      pw.z = pack_bf16x2(sv[8 * c + 4] * vsc, sv[8 * c + 5] * vsc);
+      pw.w = pack_bf16x2(sv[8 * c + 6] * vsc, sv[8 * c + 7] * vsc);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* vp = &sm.vt[buf][(db * 32 + col) * VS + c * kPage + half * 4];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+        const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
+                                                          acc[db], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < n_kt) stage_store<D, FP8>(st, sm, buf ^ 1, kt + 1, ctx, tid);
+    __syncthreads();
+  }
+
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + qrow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w.x = pack_bf16x2(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv);
+      w.y = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + db * 32 + 8 * j + 4 * half) = w;
+    }
+  if (half == 0 && a.lse) a.lse[qrow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+}
+
+// fp32 pools: one wave per (query row, query head); lane owns features lane
+// and lane + 64; plain FMA arithmetic, online softmax one key at a time.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave, h = blockIdx.y, b = blockIdx.z;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, g = h / G;
+  const int q0 = a.cu_q_lens[b];
+  const int qlen = a.cu_q_lens[b + 1] - q0;
+  if (i >= qlen) return;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  const int pos = ctx - qlen + i;
+  const int t_end = a.causal ? min(ctx, pos + 1) : ctx;
+  constexpr int NPL = D / 64;
+  const int64_t row = static_cast<int64_t>(q0 + i) * Hq + h;
+  const float* qp = static_cast<const float*>(a.q) + row * D;
+  float q[NPL], o[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    q[j] = qp[lane + 64 * j];
+    o[j] = 0.f;
+  }
+  const float* kb = static_cast<const float*>(a.k);
+  const float* vb = static_cast<const float*>(a.v);
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const float sc = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < t_end; ++t) {
+    const int32_t phys = bt[t / kPage];
+    if (phys < 0 || phys >= a.num_blocks) continue;
+    const int64_t chunk = (static_cast<int64_t>(phys) * Hkv + g) * kPage * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) dot += q[j] * kb[chunk + (t % kPage) * D + lane + 64 * j];
+    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s);
+    const float s2 = dot * sc;
+    const float m_new = fmaxf(m, s2);
+    const float alpha = fast_exp2(m - m_new);
+    const float pr = fast_exp2(s2 - m_new);
+    l = l * alpha + pr;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      o[j] = o[j] * alpha + pr * vb[chunk + (lane + 64 * j) * kPage + t % kPage];
+    m = m_new;
+  }
+  const bool empty = !(l > 0.f);
+  float* op = static_cast<float*>(a.o) + row * D;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) op[lane + 64 * j] = empty ? 0.f : o[j] / l;
+  if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+}
+
+template <int D>
+hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
+  if (a.kv_dtype == PA_F32) {
+    const dim3 grid((a.max_q_len + 3) / 4, a.num_q_heads, a.num_seqs);
+    prefill_f32_kernel<D><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int TQ = kRows / G;
+  const int n_tiles = (a.max_q_len + TQ - 1) / TQ;
+  const dim3 grid(a.num_seqs * a.num_kv_heads, n_tiles);
+  if (a.kv_dtype == PA_FP8_E4M3)
+    prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
+  else
+    prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t st) {
+  return a.head_dim == 64 ? launch_prefill_d<64>(a, st) : launch_prefill_d<128>(a, st);
+}
+
+}  // namespace pa

@@ -1,0 +1,165 @@
+"""Host-side tests of the C ABI (no GPU needed; nothing here launches a kernel).
+
+The library must load and export every function include/pa.h declares; the
+block allocator is pure host code; argument checks must return an error
+status before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_softmax_paged_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pa.h but not exported"
+    assert sorted(pa.EXPORTED) == names
+
+
+def test_status_strings_and_version():
+    assert pa.abi_version() == 1
+    assert pa.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert pa.status_string(s) and pa.status_string(s) != "unknown status"
+    assert pa.status_string(7) == "unknown status"
+
+
+def test_allocator_alloc_free_refcount():
+    a = pa.BlockAllocator(4)
+    assert a.num_free() == 4
+    ids = [a.alloc() for _ in range(4)]
+    assert ids == [0, 1, 2, 3]
+    assert a.alloc() == -1                       # exhausted
+    a.incref(2)
+    a.incref(2)
+    assert a.refcount(2) == 3
+    a.decref(2)
+    a.decref(2)
+    assert a.refcount(2) == 1 and a.num_free() == 0
+    a.decref(2)
+    assert a.refcount(2) == 0 and a.num_free() == 1
+    with pytest.raises(pa.PAError) as e:
+        a.decref(2)                              # double free
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+    with pytest.raises(pa.PAError):
+        a.incref(2)                              # sharing a free block
+    with pytest.raises(pa.PAError):
+        a.decref(17)
+    assert a.refcount(-1) == -1 and a.refcount(4) == -1
+    assert a.alloc() == 2                        # lowest free id first
+
+
+def test_allocator_shared_prefix_lifecycle():
+    """16 sequences share 4 prefix blocks (one reference each) and own 2 each;
+    ending every sequence returns every block."""
+    a = pa.BlockAllocator(64)
+    prefix = [a.alloc() for _ in range(4)]
+    for _ in range(15):
+        for p in prefix:
+            a.incref(p)
+    own = [[a.alloc(), a.alloc()] for _ in range(16)]
+    assert all(a.refcount(p) == 16 for p in prefix)
+    assert a.num_free() == 64 - 4 - 32
+    for s in range(16):
+        for p in prefix + own[s]:
+            a.decref(p)
+    assert a.num_free() == 64
+    with pytest.raises(ValueError):
+        pa.BlockAllocator(0)
+
+
+class _FakePool:
+    """A pool descriptor pointing at fake (never dereferenced) addresses."""
+
+    def __init__(self, **kw):
+        f = dict(k=0x1000, v=0x2000, k_scale=0x3000, v_scale=0x4000, num_blocks=8,
+                 num_kv_heads=2, head_dim=128, block_size=16, kv_dtype=pa.PA_BF16)
+        f.update(kw)
+        self._c = pa._Pool(f["k"], f["v"], f["k_scale"], f["v_scale"], f["num_blocks"],
+                           f["num_kv_heads"], f["head_dim"], f["block_size"], f["kv_dtype"])
+        self.c = ctypes.byref(self._c)
+
+
+def _prefill(pool, **kw):
+    a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, cu=0x8000, ctx=0x9000,
+             bt=0xa000, stride=4, B=2, Hq=8, max_q=64, max_ctx=64, scale=0.1, causal=1)
+    a.update(kw)
+    return pa._prefill(pool.c, a["q"], a["q_dtype"], a["o"], a["lse"], a["cu"], a["ctx"], a["bt"],
+                       a["stride"], a["B"], a["Hq"], a["max_q"], a["max_ctx"], a["scale"],
+                       a["causal"], None)
+
+
+def _decode(pool, **kw):
+    a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, ctx=0x9000, bt=0xa000,
+             stride=4, B=2, Hq=8, max_ctx=64, scale=0.1, splits=2, ws=0, ws_bytes=0)
+    a.update(kw)
+    return pa._decode(pool.c, a["q"], a["q_dtype"], a["o"], a["lse"], a["ctx"], a["bt"],
+                      a["stride"], a["B"], a["Hq"], a["max_ctx"], a["scale"], a["splits"],
+                      a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("pool_kw,call_kw,want", [
+    (dict(block_size=32), {}, pa.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), {}, pa.PA_ERR_UNSUPPORTED),
+    (dict(k=0), {}, pa.PA_ERR_INVALID_ARG),
+    (dict(k=0x1008), {}, pa.PA_ERR_INVALID_ARG),             # misaligned pool
+    (dict(kv_dtype=pa.PA_FP8_E4M3, k_scale=0), {}, pa.PA_ERR_INVALID_ARG),
+    ({}, dict(q_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),    # f32 q with bf16 pool
+    ({}, dict(Hq=6), pa.PA_ERR_UNSUPPORTED),                 # group of 3
+    ({}, dict(Hq=7), pa.PA_ERR_INVALID_ARG),                 # not a multiple of Hkv
+    ({}, dict(q=0x5004), pa.PA_ERR_INVALID_ARG),             # misaligned q
+    ({}, dict(stride=3), pa.PA_ERR_INVALID_ARG),             # table narrower than max ctx
+    ({}, dict(max_q=65), pa.PA_ERR_INVALID_ARG),             # max_q_len > max_ctx_len
+    ({}, dict(cu=0), pa.PA_ERR_INVALID_ARG),
+    ({}, dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    ({}, dict(B=-1), pa.PA_ERR_INVALID_ARG),
+])
+def test_prefill_rejects_bad_arguments(pool_kw, call_kw, want):
+    assert _prefill(_FakePool(**pool_kw), **call_kw) == want
+
+
+def test_empty_batch_is_a_no_op():
+    assert _prefill(_FakePool(), B=0) == pa.PA_OK
+    assert _decode(_FakePool(), B=0) == pa.PA_OK
+
+
+def test_decode_workspace_checks():
+    need = pa.decode_workspace_bytes(2, 8, 128, 2)
+    assert need >= 2 * 8 * 2 * (128 + 1) * 4
+    assert pa.decode_workspace_bytes(2, 8, 128, 1) == 0
+    assert _decode(_FakePool(), ws=0) == pa.PA_ERR_WORKSPACE
+    assert _decode(_FakePool(), ws=0x10000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
+    assert _decode(_FakePool(), ws=0x10008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG
+    assert _decode(_FakePool(), splits=-1) == pa.PA_ERR_INVALID_ARG
+
+
+def test_decode_split_heuristic():
+    # long context, few sequences: many splits; short contexts: few
+    assert pa.decode_num_splits(8, 8, 32768) == 16
+    assert pa.decode_num_splits(1, 1, 100) == 1
+    assert 1 <= pa.decode_num_splits(32, 8, 2048) <= 16
+    assert pa.decode_num_splits(0, 8, 100) == 1
+
+
+def test_write_kv_checks():
+    p = _FakePool()
+    assert pa._write(p.c, 0x1000, 0x2000, pa.PA_F32, 0x3000, 4, None, 0, None) == pa.PA_ERR_UNSUPPORTED
+    assert pa._write(p.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, -1, None, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert pa._write(p.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, 0, None, 0, None) == pa.PA_OK
+    f = _FakePool(kv_dtype=pa.PA_FP8_E4M3)
+    assert pa._write_ws(f.c) == 2 * 4 * 8
+    assert pa._write(f.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, 4, None, 0, None) == pa.PA_ERR_WORKSPACE

@@ -1,0 +1,306 @@
+"""GPU parity: the HIP library against the float64 oracle, on the same seeded
+inputs, through the C ABI.  Bit-exact for the pool write and the block-table
+gather; within the stated tolerance for attention (max |error| <= 1e-5 for
+fp32, 2e-2 for bf16, 6e-2 for an fp8 pool), for outputs and logsumexps.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+pa = pytest.importorskip("online_softmax_paged_amd")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _check_call(wl, call, pool, opool, num_splits=0, rows=None):
+    dc = H.DeviceCall(wl, call)
+    o, lse = dc.run(pool, num_splits=num_splits)
+    torch.cuda.synchronize()
+    if rows is None:
+        ro, rl = H.oracle_call(opool, wl, call)
+        eo, el = H.max_err(o, lse, ro, rl)
+    else:
+        ro, rl = H.oracle_rows(opool, wl, call, rows)
+        t = torch.tensor([r[0] for r in rows])
+        h = torch.tensor([r[1] for r in rows])
+        eo, el = H.max_err(o.cpu()[t, h], lse.cpu()[t, h], ro, rl)
+    tol = H.tolerance(wl)
+    _log(f"  {wl.name} {call.kind}: max|dO|={eo:.3e} max|dLSE|={el:.3e} tol={tol}")
+    assert eo <= tol and el <= tol, (eo, el, tol)
+    return o, lse
+
+
+# ------------------------------------------------------------ pool write / gather
+@pytest.mark.parametrize("kv_dtype,src", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16"),
+                                          ("fp8", "f32")])
+def test_write_kv_bit_exact(kv_dtype, src):
+    wl = workloads.small("decode", kv_dtype=kv_dtype, q_dtype="f32" if kv_dtype == "f32" else "bf16",
+                         num_q_heads=8, num_kv_heads=4, head_dim=128,
+                         ctx_lens=(1, 15, 16, 17, 250, 513), src_dtype=src, seed=31)
+    _log(f"write_kv {kv_dtype} <- {src}")
+    pool = H.device_pool(wl)
+    opool = H.oracle_pool(wl)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(pool.k), opool.k)
+    assert np.array_equal(_bits(pool.v), opool.v)
+    if kv_dtype == "fp8":
+        assert np.array_equal(_bits(pool.k_scale), opool.k_scale.view(np.uint32))
+        assert np.array_equal(_bits(pool.v_scale), opool.v_scale.view(np.uint32))
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_gather_kv_bit_exact(kv_dtype):
+    wl = workloads.small("decode", kv_dtype=kv_dtype, q_dtype="f32" if kv_dtype == "f32" else "bf16",
+                         num_q_heads=4, num_kv_heads=2, head_dim=64, ctx_lens=(3, 16, 40, 333),
+                         seed=32)
+    _log(f"gather_kv {kv_dtype}")
+    pool = H.device_pool(wl)
+    call = wl.calls[0]
+    k, v = pa.gather_kv(pool, call.block_table.cuda(), call.ctx_lens.cuda(), int(call.ctx_lens.max()))
+    kb, vb = _bits(k), _bits(v)
+    opool = H.oracle_pool(wl)
+    off = 0
+    for b, c in enumerate(wl.ctx_lens):
+        for t in range(c):
+            p = int(call.block_table[b, t // 16])
+            assert np.array_equal(kb[off + t], opool.k[p, :, t % 16, :])
+            assert np.array_equal(vb[off + t], opool.v[p, :, :, t % 16])
+        off += c
+
+
+# ------------------------------------------------------------ decode parity
+DECODE_CASES = [
+    ("f32", "f32", 64, 1, 1, (1, 15, 16, 17, 256)),
+    ("f32", "f32", 128, 4, 2, (33, 200)),
+    ("bf16", "bf16", 128, 8, 2, (1, 15, 16, 17, 100, 300, 1000)),
+    ("bf16", "bf16", 128, 64, 8, (500, 2000)),
+    ("bf16", "bf16", 64, 16, 16, (77, 300)),
+    ("bf16", "bf16", 128, 32, 2, (129, 40)),
+    ("bf16", "bf16", 64, 4, 2, (600,)),
+    ("fp8", "bf16", 128, 8, 2, (1, 17, 300, 1000)),
+    ("fp8", "bf16", 64, 16, 2, (50, 400)),
+]
+
+
+@pytest.mark.parametrize("kv,qd,D,Hq,Hkv,ctx", DECODE_CASES)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_parity(kv, qd, D, Hq, Hkv, ctx, splits):
+    _log(f"decode kv={kv} D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} splits={splits}")
+    wl = workloads.small("decode", kv_dtype=kv, q_dtype=qd, num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, ctx_lens=ctx, seed=40 + D + Hq)
+    _check_call(wl, wl.calls[0], H.device_pool(wl), H.oracle_pool(wl), num_splits=splits)
+
+
+# ------------------------------------------------------------ prefill parity
+PREFILL_CASES = [
+    # kv, q, D, Hq, Hkv, ctx_lens, q_lens (None = whole sequence), causal
+    ("f32", "f32", 64, 1, 1, (256, 17), None, True),
+    ("f32", "f32", 128, 4, 2, (100, 40), (30, 40), True),
+    ("bf16", "bf16", 128, 8, 2, (300, 1, 17, 64, 129), None, True),
+    ("bf16", "bf16", 128, 8, 2, (700, 300), (45, 300), True),
+    ("bf16", "bf16", 128, 8, 2, (200, 90), (77, 90), False),
+    ("bf16", "bf16", 64, 16, 16, (250, 33), None, True),
+    ("bf16", "bf16", 128, 64, 8, (300,), None, True),
+    ("bf16", "bf16", 128, 32, 2, (97, 40), (50, 40), True),
+    ("bf16", "bf16", 64, 4, 2, (333,), None, True),
+    ("fp8", "bf16", 128, 8, 2, (400, 60), (256, 60), True),
+    ("fp8", "bf16", 64, 16, 2, (150,), None, True),
+]
+
+
+@pytest.mark.parametrize("kv,qd,D,Hq,Hkv,ctx,ql,causal", PREFILL_CASES)
+def test_prefill_parity(kv, qd, D, Hq, Hkv, ctx, ql, causal):
+    _log(f"prefill kv={kv} D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} q={ql} causal={causal}")
+    wl = workloads.small("prefill", kv_dtype=kv, q_dtype=qd, num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, ctx_lens=ctx, q_lens=ql, seed=50 + D + Hq)
+    wl.calls[0].causal = causal
+    _check_call(wl, wl.calls[0], H.device_pool(wl), H.oracle_pool(wl))
+
+
+# ------------------------------------------------------------ the five named workloads
+@functools.lru_cache(maxsize=1)
+def _named(k):
+    wl = workloads.NAMED[k]()
+    return wl, H.oracle_pool(wl)
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 5])
+def test_named_workload_full(k):
+    _log(f"named workload {k}")
+    wl, opool = _named(k)
+    pool = H.device_pool(wl)
+    for call in wl.calls:
+        _check_call(wl, call, pool, opool)
+
+
+def test_named_prefill_4x4096_sampled():
+    """Full-size causal prefill in the benchmark's launch configuration; the
+    oracle checks sampled rows one by one."""
+    _log("named workload 3 (sampled rows)")
+    wl, opool = _named(3)
+    pool = H.device_pool(wl)
+    call = wl.calls[0]
+    rows = H.sample_rows(call, wl.num_q_heads, 96, seed=3)
+    _check_call(wl, call, pool, opool, rows=rows)
+
+
+# ------------------------------------------------------------ invariants
+def _run_both(wl, pool):
+    return [H.DeviceCall(wl, c).run(pool) for c in wl.calls]
+
+
+def test_block_relabelling_is_bit_identical():
+    """Moving every page to another physical id (and remapping the tables)
+    leaves outputs bit-identical: the math does not depend on where pages live."""
+    _log("relabel")
+    for kind in ("decode", "prefill"):
+        wl = workloads.small(kind, num_q_heads=8, num_kv_heads=2, ctx_lens=(300, 45, 129), seed=60)
+        r1 = _run_both(wl, H.device_pool(wl))
+        perm = torch.randperm(wl.num_blocks, generator=torch.Generator().manual_seed(5)).to(torch.int32)
+        wl.slot_mapping = perm[(wl.slot_mapping // 16).long()] * 16 + wl.slot_mapping % 16
+        for c in wl.calls:
+            bt = c.block_table.clone()
+            bt[bt >= 0] = perm[bt[bt >= 0].long()]
+            c.block_table = bt
+        r2 = _run_both(wl, H.device_pool(wl))
+        for (o1, l1), (o2, l2) in zip(r1, r2):
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_shared_prefix_equals_private_copies():
+    """Sequences reading one shared physical prefix give bit-identical results
+    to the same sequences with private copies of those bytes."""
+    _log("shared prefix")
+    mk = lambda shared: workloads.build(
+        "p", kv_dtype="fp8", q_dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+        ctx_lens=[200, 200, 200], shared_prefix=shared,
+        calls=[workloads.Call("decode", [0, 1, 2], [1, 1, 1])], seed=61)
+    wl_s = mk(64)
+    pool_s = H.device_pool(wl_s)
+    # private copies: duplicate the shared pages into fresh physical blocks
+    wl_p = mk(64)
+    extra = 3 * 4
+    pool_p = pa.KVPool(wl_s.num_blocks + extra, 2, 128, "fp8")
+    pool_p.k[: wl_s.num_blocks] = pool_s.k
+    pool_p.v[: wl_s.num_blocks] = pool_s.v
+    pool_p.k_scale[: wl_s.num_blocks] = pool_s.k_scale
+    pool_p.v_scale[: wl_s.num_blocks] = pool_s.v_scale
+    bt = wl_p.calls[0].block_table.clone()
+    nid = wl_s.num_blocks
+    for b in range(3):
+        for j in range(4):
+            src = int(bt[b, j])
+            pool_p.k[nid] = pool_s.k[src]
+            pool_p.v[nid] = pool_s.v[src]
+            pool_p.k_scale[nid] = pool_s.k_scale[src]
+            pool_p.v_scale[nid] = pool_s.v_scale[src]
+            bt[b, j] = nid
+            nid += 1
+    assert len(set(bt[:, :4].flatten().tolist())) == 12
+    wl_p.calls[0].block_table = bt
+    o1, l1 = H.DeviceCall(wl_s, wl_s.calls[0]).run(pool_s)
+    o2, l2 = H.DeviceCall(wl_p, wl_p.calls[0]).run(pool_p)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeat_runs_are_bitwise_equal_and_splits_agree():
+    _log("determinism / splits")
+    wl = workloads.small("decode", num_q_heads=16, num_kv_heads=2, ctx_lens=(2000, 900, 31), seed=62)
+    pool = H.device_pool(wl)
+    dc = H.DeviceCall(wl, wl.calls[0])
+    for s in (1, 2, 5, 16):
+        a = dc.run(pool, num_splits=s)
+        b = dc.run(pool, num_splits=s)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    ro, rl = H.oracle_call(H.oracle_pool(wl), wl, wl.calls[0])
+    for s in (1, 2, 3, 7, 16, 125):
+        eo, el = H.max_err(*dc.run(pool, num_splits=s), ro, rl)
+        assert eo <= 2e-2 and el <= 1e-4, (s, eo, el)
+    wl2 = workloads.small("prefill", num_q_heads=8, num_kv_heads=2, ctx_lens=(500, 70), seed=63)
+    pool2 = H.device_pool(wl2)
+    dc2 = H.DeviceCall(wl2, wl2.calls[0])
+    a, b = dc2.run(pool2), dc2.run(pool2)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_table_entries_past_the_end_are_never_read():
+    """Entries after a sequence's last page: -1 (default) or a wild id NB+7."""
+    _log("table poison")
+    for kind in ("decode", "prefill"):
+        wl = workloads.small(kind, num_q_heads=8, num_kv_heads=2, ctx_lens=(300, 20, 170), seed=64)
+        pool = H.device_pool(wl)
+        r1 = _run_both(wl, pool)
+        for c in wl.calls:
+            c.block_table[c.block_table < 0] = wl.num_blocks + 7
+        r2 = _run_both(wl, pool)
+        for (o1, l1), (o2, l2) in zip(r1, r2):
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_matches_last_prefill_row():
+    """Decode of the last position's query equals prefill's last row (both
+    against the oracle, and against each other within the bf16 tolerance)."""
+    _log("decode vs prefill last row")
+    wl = workloads.small("prefill", num_q_heads=8, num_kv_heads=2, ctx_lens=(333, 64), seed=65)
+    pool = H.device_pool(wl)
+    call = wl.calls[0]
+    o_p, l_p = H.DeviceCall(wl, call).run(pool)
+    last = call.cu_q_lens[1:] - 1
+    dq = call.q[last.long()].contiguous().cuda()
+    o_d, l_d = pa.decode(pool, dq, call.ctx_lens.cuda(), call.block_table.cuda(), wl.scale)
+    assert (o_d.float() - o_p[last.long().cuda()].float()).abs().max().item() <= 2e-2
+    assert (l_d - l_p[last.long().cuda()]).abs().max().item() <= 1e-4
+
+
+def test_causal_first_row_is_v0_exactly():
+    _log("first row")
+    wl = workloads.small("prefill", num_q_heads=4, num_kv_heads=2, ctx_lens=(64,), seed=66)
+    pool = H.device_pool(wl)
+    o, lse = H.DeviceCall(wl, wl.calls[0]).run(pool)
+    v0 = wl.v_src[0]                       # token 0, [Hkv, D]
+    for h in range(4):
+        assert torch.equal(o[0, h].cpu(), v0[h // 2])
+        ref = wl.scale * float(wl.calls[0].q[0, h].double() @ wl.k_src[0, h // 2].double())
+        assert abs(lse[0, h].item() - ref) <= 1e-4
+
+
+def test_constant_v_gives_the_constant():
+    _log("constant V")
+    wl = workloads.small("prefill", num_q_heads=8, num_kv_heads=2, ctx_lens=(300, 33), seed=67)
+    c = torch.linspace(-3, 3, 128).to(torch.bfloat16)
+    wl.v_src = c.reshape(1, 1, 128).expand_as(wl.v_src).contiguous()
+    pool = H.device_pool(wl)
+    o, _ = H.DeviceCall(wl, wl.calls[0]).run(pool)
+    assert (o.float().cpu() - c.float()).abs().max().item() <= 2e-2
+
+
+def test_empty_batch_and_validation():
+    wl = workloads.small("decode", num_q_heads=8, num_kv_heads=2, ctx_lens=(40,), seed=68)
+    pool = H.device_pool(wl)
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    e = torch.empty((0,), dtype=torch.int32, device="cuda")
+    o, lse = pa.decode(pool, q, e, torch.zeros((0, 3), dtype=torch.int32, device="cuda"), 0.1,
+                       max_ctx_len=40)
+    assert o.numel() == 0
+    bad = wl.calls[0].block_table.clone().cuda()
+    bad[0, 0] = wl.num_blocks
+    with pytest.raises(ValueError):
+        pa.decode(pool, wl.calls[0].q.cuda(), wl.calls[0].ctx_lens.cuda(), bad, 0.1, validate=True)
