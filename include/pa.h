@@ -140,7 +140,8 @@ pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32
  *   lse : float [cu_q_lens[num_seqs], num_q_heads] natural-log logsumexp of the
  *         scaled scores of each row (device, written; may be NULL)
  *   cu_q_lens : int32 [num_seqs + 1]; ctx_lens : int32 [num_seqs] (device)
- * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).  scale must be
+ * finite and > 0 (usually 1/sqrt(head_dim)).
  * Supported: q_dtype PA_F32 with an f32 pool; q_dtype PA_BF16 with a bf16 or
  * fp8 pool.  head_dim 64 or 128; num_q_heads / num_kv_heads in {1,2,4,8,16}.
  * q and o must be 16-byte aligned.

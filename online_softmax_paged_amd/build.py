@@ -20,6 +20,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "kv_cache.hip", "decode.hip", "prefill.hip", "allocator.cpp"]
 
+# Keep MFMA accumulators in ordinary VGPRs so the softmax can rescale them
+# without copies to and from the accumulation registers.
+PER_FILE = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,7 +37,7 @@ def _compile(src: str) -> str:
         cmd = ["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"),
                "-c", path, "-o", out]
     else:
-        cmd = [HIPCC] + HIP_FLAGS + ["-c", path, "-o", out]
+        cmd = [HIPCC] + HIP_FLAGS + PER_FILE.get(src, []) + ["-c", path, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(x for x in (r.stdout + r.stderr).splitlines() if noise not in x)

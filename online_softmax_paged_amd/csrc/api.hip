@@ -44,7 +44,7 @@ pa_status check_attn(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, co
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return PA_ERR_UNSUPPORTED;
   if (max_ctx_len < 1) return PA_ERR_INVALID_ARG;
   if (bt_stride < (max_ctx_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(AttnArgs a) {
     const float lse = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
     const int64_t row = static_cast<int64_t>(b) * Hq + g * G + hd;
     if (S == 1) {
-      static_cast<uint16_t*>(a.o)[row * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(out));
+      static_cast<uint16_t*>(a.o)[row * D + d] = to_bf16_bits(out);
       if (d == 0 && a.lse) a.lse[row] = lse;
     } else {
       a.ws_o[(row * S + split) * D + d] = out;
@@ -290,6 +290,10 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
 }
 
 // One wave per (sequence, query head): logsumexp-weighted sum of the ranges.
+// The range weights are computed by the lanes in parallel (lane s holds range
+// s, up to 64 per pass) and broadcast with readlane, so the partial outputs of
+// all ranges are independent loads.  Empty ranges carry lse = -inf, weight 0
+// and a zero partial output.
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -299,30 +303,52 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   const int S = a.num_splits;
   const float* ls = a.ws_lse + row * S;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ls[s]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ls[s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   constexpr int NPL = D / 64;
-  float o[NPL];
+  float acc[NPL];
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) o[j] = 0.f;
+  for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
   float W = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float lsv = ls[s];
-      if (lsv == -INFINITY) continue;
-      const float w = fast_exp2((lsv - M) * kLog2e);
-      W += w;
-      const float* op = a.ws_o + (row * S + s) * D;
+  const float Mu = M == -INFINITY ? 0.f : M;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    const float lsv = s < S ? ls[s] : -INFINITY;
+    const float w = lsv == -INFINITY ? 0.f : fast_exp2((lsv - Mu) * kLog2e);
+    W += w;
+    const int n = min(64, S - s0);
+    const float* op = a.ws_o + (row * S + s0) * D + lane;
+    const int wbits = __builtin_bit_cast(int, w);
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {  // 8 ranges' loads in flight at once
+      float x[8][NPL];
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) o[j] += w * op[lane + 64 * j];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) x[u][j] = op[(i + u) * D + 64 * j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, i + u));
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) acc[j] += wi * x[u][j];
+      }
+    }
+    for (; i < n; ++i) {
+      const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, i));
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[j] += wi * op[i * D + 64 * j];
     }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
   const bool empty = !(W > 0.f);
+  const float inv = empty ? 0.f : 1.f / W;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const float out = empty ? 0.f : o[j] / W;
+    const float out = acc[j] * inv;
     if constexpr (sizeof(OutT) == 2)
-      static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] =
-          static_cast<uint16_t>(f32_to_bf16_bits(out));
+      static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] = to_bf16_bits(out);
     else
       static_cast<float*>(a.o)[row * D + lane + 64 * j] = out;
   }

@@ -24,27 +24,17 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
-// float -> bfloat16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Two floats -> two bf16 packed in one dword (low = a), round to nearest even.
+// Two floats -> two bf16 packed in one dword (low = a), round to nearest even
+// (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// fp8 E4M3 (OCP) byte -> float, via the hardware converter.
-__device__ __forceinline__ float fp8_to_f32(uint32_t word, int byte) {
-  switch (byte) {
-    case 0: return __builtin_amdgcn_cvt_f32_fp8(word, 0);
-    case 1: return __builtin_amdgcn_cvt_f32_fp8(word, 1);
-    case 2: return __builtin_amdgcn_cvt_f32_fp8(word, 2);
-    default: return __builtin_amdgcn_cvt_f32_fp8(word, 3);
-  }
+__device__ __forceinline__ uint16_t to_bf16_bits(float a) {
+  return static_cast<uint16_t>(pack_bf16x2(a, 0.f));
 }
 
 // Four fp8 codes in a dword -> four bf16 packed in two dwords (exact: every
@@ -61,6 +51,14 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The value held by lane l ^ 32 (v_permlane32_swap, no LDS round trip).
+__device__ __forceinline__ float swap_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // lanes 0-31 find their partner in the second result, lanes 32-63 in the first
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // ----------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.

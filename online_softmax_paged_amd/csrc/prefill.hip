@@ -36,58 +36,68 @@ struct Smem {
   uint16_t vt[2][D * VS];
 };
 
-// Global -> register staging of one 32-key tile.
+// The two physical pages of one 32-key tile (uniform across the workgroup),
+// looked up two tiles ahead so the block-table read latency stays hidden.
+struct TilePages {
+  int32_t phys[2];
+  bool ok[2];        // page holds keys of this sequence and its id is valid
+  float ks[2], vs[2];  // fp8 page scales (1 for other pools)
+};
+
+template <bool FP8>
+__device__ __forceinline__ TilePages pages_of(const AttnArgs& a, const int32_t* bt, int t,
+                                              int n_pages) {
+  TilePages tp;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int pidx = 2 * t + j;
+    int32_t phys = pidx < n_pages ? bt[pidx] : -1;
+    phys = __builtin_amdgcn_readfirstlane(phys);
+    const bool ok = phys >= 0 && phys < a.num_blocks;
+    tp.phys[j] = phys;
+    tp.ok[j] = ok;
+    tp.ks[j] = 1.f;
+    tp.vs[j] = 1.f;
+    if constexpr (FP8) {
+      tp.ks[j] = ok ? a.k_scale[phys] : 0.f;
+      tp.vs[j] = ok ? a.v_scale[phys] : 0.f;
+    }
+  }
+  return tp;
+}
+
+// Global -> register staging of one 32-key tile: each thread moves 16-byte
+// chunks of the two K pages and the two V pages.  Which page a chunk belongs
+// to is uniform per wave, so the page checks are scalar branches.
 template <int D, bool FP8>
 struct Stage {
-  // bf16: K 2 chunks of 16 B, V 2 chunks of 16 B per thread (D=128).
-  // fp8:  K 1 chunk, V 1 chunk per thread (16 fp8 = 16 B).
-  static constexpr int KCH = FP8 ? (kKeys * D / 16 + 255) / 256 : (kKeys * D / 8 + 255) / 256;
-  static constexpr int VCH = KCH;
+  static constexpr int CPP = FP8 ? kPage * D / 16 : kPage * D / 8;  // chunks per page
+  static constexpr int KCH = (2 * CPP + 255) / 256;
   u32x4 k[KCH];
-  u32x4 v[VCH];
+  u32x4 v[KCH];
 };
 
 template <int D, bool FP8>
 __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const AttnArgs& a, int g,
-                                           const int32_t* bt, int kt, int ctx, int tid) {
-  const int Hkv = a.num_kv_heads;
-  if constexpr (!FP8) {
-    constexpr int CPP = kPage * D / 8;  // 16-byte chunks per page
+                                           const TilePages& tp, int tid) {
+  constexpr int CPP = Stage<D, FP8>::CPP;
+  constexpr int ES = FP8 ? 16 : 8;  // elements per chunk
 #pragma unroll
-    for (int r = 0; r < st.KCH; ++r) {
-      const int e = r * 256 + tid;
-      const int pg = e / CPP, within = e % CPP;
-      const int tok = kt * kKeys + pg * kPage;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (e < 2 * CPP && tok < ctx) {
-        const int32_t phys = bt[tok / kPage];
-        if (phys >= 0 && phys < a.num_blocks) {
-          const int64_t base = (static_cast<int64_t>(phys) * Hkv + g) * (kPage * D);
-          kv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + base + within * 8);
-          vv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + base + within * 8);
-        }
-      }
-      st.k[r] = kv;
-      st.v[r] = vv;
-    }
-  } else {
-    constexpr int CPP = kPage * D / 16;
-#pragma unroll
-    for (int r = 0; r < st.KCH; ++r) {
-      const int e = r * 256 + tid;
-      const int pg = e / CPP, within = e % CPP;
-      const int tok = kt * kKeys + pg * kPage;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (e < 2 * CPP && tok < ctx) {
-        const int32_t phys = bt[tok / kPage];
-        if (phys >= 0 && phys < a.num_blocks) {
-          const int64_t base = (static_cast<int64_t>(phys) * Hkv + g) * (kPage * D);
-          kv = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k) + base + within * 16);
-          vv = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) + base + within * 16);
-        }
-      }
-      st.k[r] = kv;
-      st.v[r] = vv;
+  for (int r = 0; r < Stage<D, FP8>::KCH; ++r) {
+    const int e = min(r * 256 + tid, 2 * CPP - 1);
+    const int pg = e / CPP, within = e % CPP;
+    // Loads are unconditional so they stay in flight across the tile's math;
+    // a page that is not part of the sequence reads physical page 0 instead
+    // (always a valid address) and is zeroed when stored to LDS.
+    const bool ok = pg ? tp.ok[1] : tp.ok[0];
+    const int32_t phys = ok ? (pg ? tp.phys[1] : tp.phys[0]) : 0;
+    const int64_t base = (static_cast<int64_t>(phys) * a.num_kv_heads + g) * (kPage * D);
+    if constexpr (FP8) {
+      st.k[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k) + base + within * ES);
+      st.v[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) + base + within * ES);
+    } else {
+      st.k[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + base + within * ES);
+      st.v[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + base + within * ES);
     }
   }
 }
@@ -98,26 +108,31 @@ __device__ __forceinline__ uint32_t zero_lo_hi(uint32_t w, bool lo_dead, bool hi
   return w;
 }
 
+// Register -> LDS.  Slots at or past the context end are written as zeros so
+// that unspecified pool bytes (possibly NaN) never meet a zero probability.
 template <int D, bool FP8>
 __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm, int buf, int kt,
-                                            int ctx, int tid) {
+                                            int ctx, const TilePages& tp, int tid) {
   constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
-  if constexpr (!FP8) {
-    constexpr int CPP = kPage * D / 8;
+  constexpr int CPP = Stage<D, FP8>::CPP;
 #pragma unroll
-    for (int r = 0; r < st.KCH; ++r) {
-      const int e = r * 256 + tid;
-      if (e >= 2 * CPP) break;
-      const int pg = e / CPP, within = e % CPP;
+  for (int r = 0; r < Stage<D, FP8>::KCH; ++r) {
+    const int e = r * 256 + tid;
+    if (e >= 2 * CPP) break;
+    const int pg = e / CPP, within = e % CPP;
+    // first token of this page; a page that is not part of the sequence is
+    // treated as lying past the context end, so all of it is zeroed
+    const int page_tok = (pg ? tp.ok[1] : tp.ok[0]) ? kt * kKeys + pg * kPage : ctx;
+    if constexpr (!FP8) {
       // K chunk: token within / (D/8), features (within % (D/8)) * 8
       const int tk = within / (D / 8), dc = within % (D / 8);
       const int key = pg * kPage + tk;
       u32x4 kv = st.k[r];
-      if (kt * kKeys + key >= ctx) kv = u32x4{0, 0, 0, 0};
+      if (page_tok + tk >= ctx) kv = u32x4{0, 0, 0, 0};
       *reinterpret_cast<u32x4*>(&sm.k[buf][key * KS + dc * 8]) = kv;
       // V^T chunk: feature within / 2, tokens (within % 2) * 8 .. + 8
-      const int d = within >> 1, half = within & 1;
-      const int t0 = kt * kKeys + pg * kPage + half * 8;
+      const int d = within >> 1, hf = within & 1;
+      const int t0 = page_tok + hf * 8;
       u32x4 vv = st.v[r];
       if (t0 + 8 > ctx) {
         vv.x = zero_lo_hi(vv.x, t0 + 0 >= ctx, t0 + 1 >= ctx);
@@ -125,17 +140,10 @@ __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm
         vv.z = zero_lo_hi(vv.z, t0 + 4 >= ctx, t0 + 5 >= ctx);
         vv.w = zero_lo_hi(vv.w, t0 + 6 >= ctx, t0 + 7 >= ctx);
       }
-      uint16_t* dst = &sm.vt[buf][d * VS + pg * kPage + half * 8];
+      uint16_t* dst = &sm.vt[buf][d * VS + pg * kPage + hf * 8];
       *reinterpret_cast<u32x2*>(dst) = u32x2{vv.x, vv.y};
       *reinterpret_cast<u32x2*>(dst + 4) = u32x2{vv.z, vv.w};
-    }
-  } else {
-    constexpr int CPP = kPage * D / 16;
-#pragma unroll
-    for (int r = 0; r < st.KCH; ++r) {
-      const int e = r * 256 + tid;
-      if (e >= 2 * CPP) break;
-      const int pg = e / CPP, within = e % CPP;
+    } else {
       // K chunk: 16 features of one token
       const int tk = within / (D / 16), dc = within % (D / 16);
       const int key = pg * kPage + tk;
@@ -143,21 +151,20 @@ __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm
       u32x2 k0 = fp8x4_to_bf16x4(kw.x), k1 = fp8x4_to_bf16x4(kw.y);
       u32x2 k2 = fp8x4_to_bf16x4(kw.z), k3 = fp8x4_to_bf16x4(kw.w);
       u32x4 ka = {k0.x, k0.y, k1.x, k1.y}, kb = {k2.x, k2.y, k3.x, k3.y};
-      if (kt * kKeys + key >= ctx) ka = kb = u32x4{0, 0, 0, 0};
+      if (page_tok + tk >= ctx) ka = kb = u32x4{0, 0, 0, 0};
       uint16_t* kd = &sm.k[buf][key * KS + dc * 16];
       *reinterpret_cast<u32x4*>(kd) = ka;
       *reinterpret_cast<u32x4*>(kd + 8) = kb;
       // V^T chunk: all 16 tokens of one feature row
       const int d = within;
-      const int t0 = kt * kKeys + pg * kPage;
       const u32x4 vw = st.v[r];
       u32x2 w[4] = {fp8x4_to_bf16x4(vw.x), fp8x4_to_bf16x4(vw.y), fp8x4_to_bf16x4(vw.z),
                     fp8x4_to_bf16x4(vw.w)};
-      if (t0 + kPage > ctx) {
+      if (page_tok + kPage > ctx) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          w[j].x = zero_lo_hi(w[j].x, t0 + 4 * j + 0 >= ctx, t0 + 4 * j + 1 >= ctx);
-          w[j].y = zero_lo_hi(w[j].y, t0 + 4 * j + 2 >= ctx, t0 + 4 * j + 3 >= ctx);
+          w[j].x = zero_lo_hi(w[j].x, page_tok + 4 * j + 0 >= ctx, page_tok + 4 * j + 1 >= ctx);
+          w[j].y = zero_lo_hi(w[j].y, page_tok + 4 * j + 2 >= ctx, page_tok + 4 * j + 3 >= ctx);
         }
       }
       uint16_t* vd = &sm.vt[buf][d * VS + pg * kPage];
@@ -189,16 +196,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   if (kmax <= 0) return;                      // inconsistent lengths: nothing visible
   const int n_kt = (kmax + kKeys - 1) / kKeys;
+  const int n_pages = (ctx + kPage - 1) / kPage;
   // Tiles whose keys are all visible to every row need no mask.
   const int first_pos = pos_base + t0;
   const int n_full = a.causal ? max(0, min((first_pos + 1) / kKeys, ctx / kKeys))
                               : ctx / kKeys;
 
-  // This lane's query row.
+  // This lane's query row, and the last key it may see.
   const int r = wave * 32 + col;
   const int tt = t0 + r / G, hg = r % G;
   const bool row_ok = tt < qlen;
   const int qpos = pos_base + tt;
+  const int key_lim = a.causal ? min(qpos, ctx - 1) : ctx - 1;
   const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
 
   bf16x8 qf[D / 16];
@@ -213,83 +222,83 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
 
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
   const float sc = a.scale * kLog2e;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, mu = 0.f;  // mu: the max used in exponents (0 while m = -inf)
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
+  TilePages cur = pages_of<FP8>(a, bt, 0, n_pages);
+  TilePages nxt = pages_of<FP8>(a, bt, 1, n_pages);
   Stage<D, FP8> st;
-  stage_load<D, FP8>(st, a, g, bt, 0, ctx, tid);
-  stage_store<D, FP8>(st, sm, 0, 0, ctx, tid);
+  stage_load<D, FP8>(st, a, g, cur, tid);
+  stage_store<D, FP8>(st, sm, 0, 0, ctx, cur, tid);
   __syncthreads();
 
   constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) stage_load<D, FP8>(st, a, g, bt, kt + 1, ctx, tid);
+    const TilePages nn = pages_of<FP8>(a, bt, kt + 2, n_pages);
+    if (kt + 1 < n_kt) stage_load<D, FP8>(st, a, g, nxt, tid);
 
     // S^T = K . Q^T  (32 keys x 32 queries)
     f32x16 s = {};
     const uint16_t* kb = &sm.k[buf][col * KS + half * 8];
+    bf16x8 kf[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-    }
-    float sc0 = sc, sc1 = sc, vs0 = 1.f, vs1 = 1.f;
-    if constexpr (FP8) {
-      const int tok = kt * kKeys;
-      const int32_t p0 = bt[tok / kPage];
-      const bool has1 = tok + kPage < ctx;
-      const int32_t p1 = has1 ? bt[tok / kPage + 1] : -1;
-      const bool ok0 = p0 >= 0 && p0 < a.num_blocks, ok1 = p1 >= 0 && p1 < a.num_blocks;
-      sc0 *= ok0 ? a.k_scale[p0] : 0.f;
-      vs0 = ok0 ? a.v_scale[p0] : 0.f;
-      sc1 *= ok1 ? a.k_scale[p1] : 0.f;
-      vs1 = ok1 ? a.v_scale[p1] : 0.f;
-    }
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
     // Score value i of this lane is key 8*(i/4) + 4*half + i%4 of the tile.
+    // Raw scores (fp8: times the page's K scale); invisible keys -> -inf.
     float sv[16];
-    const bool masked = kt >= n_full;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kt * kKeys + 8 * (i >> 2) + 4 * half + (i & 3);
-      float x = s[i] * (i < 8 ? sc0 : sc1);
-      if (masked) {
-        const bool vis = key < ctx && (!a.causal || key <= qpos);
-        x = vis ? x : -INFINITY;
-      }
-      sv[i] = x;
+    for (int i = 0; i < 16; ++i) sv[i] = FP8 ? s[i] * (i < 8 ? cur.ks[0] : cur.ks[1]) : s[i];
+    if (kt >= n_full) {
+      const int lim = key_lim - kt * kKeys - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? sv[i] : -INFINITY;
     }
-    float mt = sv[0];
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sv[i]), sv[i + 1]);
+    mt = fmaxf(mt, sv[15]);
+    mt = fmaxf(mt, swap_halves(mt));
+    const float mt_s = mt * sc;  // scaled, log2 domain (sc > 0 keeps -inf)
+    // Lazy rescaling: the running max (and with it O and l) is only moved when
+    // some row's tile max exceeds it by more than 8, so exponents stay <= 2^8
+    // and the common case skips the O rescale; the final division by l makes
+    // the result independent of which max was used.
+    if (__any(mt_s > m + 8.f)) {
+      const float m_new = fmaxf(m, mt_s);
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      m = m_new;
+      mu = m == -INFINITY ? 0.f : m;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sv[i] = fast_exp2(sv[i] - m_use);
+      sv[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -mu));
       psum += sv[i];
     }
-    l = l * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    l += psum;
 
     // O^T += V^T . P^T ; chunk c covers page c of the tile (keys 16c..16c+15)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const float vsc = c == 0 ? vs0 : vs1;
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = FP8 ? sv[8 * c + i] * cur.vs[c] : sv[8 * c + i];
       u32x4 pw;
-      pw.x = pack_bf16x2(sv[8 * c + 0] * vsc, sv[8 * c + 1] * vsc);
-      pw.y = pack_bf16x2(sv[8 * c + 2] * vsc, sv[8 * c + 3] * vsc);
-      pw.z = pack_bf16x2(sv[8 * c + 4] * vsc, sv[8 * c + 5] * vsc);
-      pw.w = pack_bf16x2(sv[8 * c + 6] * vsc, sv[8 * c + 7] * vsc);
+      pw.x = pack_bf16x2(pv[0], pv[1]);
+      pw.y = pack_bf16x2(pv[2], pv[3]);
+      pw.z = pack_bf16x2(pv[4], pv[5]);
+      pw.w = pack_bf16x2(pv[6], pv[7]);
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
@@ -301,11 +310,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
                                                           acc[db], 0, 0, 0);
       }
     }
-    if (kt + 1 < n_kt) stage_store<D, FP8>(st, sm, buf ^ 1, kt + 1, ctx, tid);
+    if (kt + 1 < n_kt) stage_store<D, FP8>(st, sm, buf ^ 1, kt + 1, ctx, nxt, tid);
     __syncthreads();
+    cur = nxt;
+    nxt = nn;
   }
 
-  l += __shfl_xor(l, 32);
+  l += swap_halves(l);
   if (!row_ok) return;
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
