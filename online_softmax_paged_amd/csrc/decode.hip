@@ -36,12 +36,20 @@ template <int D>
 struct KVFrag {
   bf16x8 k[D / 32];  // A operand of the score MFMA, one per 32-feature step
   bf16x4 v[D / 16];  // A operand of the PV MFMA, one per 16-feature block
+  float ks, vs;      // fp8 page scales
 };
 
 template <int D, bool FP8>
-__device__ __forceinline__ void load_page(KVFrag<D>& f, const void* kbase, const void* vbase,
-                                          int64_t chunk, int lane) {
+__device__ __forceinline__ void load_page(KVFrag<D>& f, const AttnArgs& a, int32_t phys, int g,
+                                          int lane) {
+  const void* kbase = a.k;
+  const void* vbase = a.v;
+  const int64_t chunk = static_cast<int64_t>(phys) * a.num_kv_heads + g;
   const int c = lane & 15, grp = lane >> 4;
+  if constexpr (FP8) {
+    f.ks = a.k_scale[phys];
+    f.vs = a.v_scale[phys];
+  }
   if constexpr (!FP8) {
     const uint16_t* kp = static_cast<const uint16_t*>(kbase) + chunk * (kPage * D);
     const uint16_t* vp = static_cast<const uint16_t*>(vbase) + chunk * (kPage * D);
@@ -110,74 +118,90 @@ __global__ __launch_bounds__(256) void decode_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  KVFrag<D> cur, nxt;
-  int p = p_begin + wave;
-  int32_t phys = p < p_end ? bt[p] : -1;
-  if (p < p_end && valid_block(phys, a.num_blocks))
-    load_page<D, FP8>(cur, a.k, a.v, static_cast<int64_t>(phys) * Hkv + g, lane);
-
-  for (; p < p_end; p += kWaves) {
-    const int pn = p + kWaves;
-    const int32_t phys_n = pn < p_end ? bt[pn] : -1;
-    if (pn < p_end && valid_block(phys_n, a.num_blocks))
-      load_page<D, FP8>(nxt, a.k, a.v, static_cast<int64_t>(phys_n) * Hkv + g, lane);
-
-    if (valid_block(phys, a.num_blocks)) {
-      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+  // Fold one page (loaded in f) into the running state.
+  auto process = [&](KVFrag<D>& f, int p, bool valid) {
+    if (!valid) return;
+    f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[ks], qf[ks], s4, 0, 0, 0);
-      float scl = sc, vscl = 1.f;
-      if constexpr (FP8) {
-        scl *= a.k_scale[phys];
-        vscl = a.v_scale[phys];
-      }
-      const int key0 = p * kPage + grp * 4;
-      float s[4];
+    for (int ks = 0; ks < D / 32; ++ks)
+      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[ks], qf[ks], s4, 0, 0, 0);
+    float scl = sc, vscl = 1.f;
+    if constexpr (FP8) {
+      scl *= f.ks;
+      vscl = f.vs;
+    }
+    const int key0 = p * kPage + grp * 4;
+    float s[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (key0 + i < ctx) ? s4[i] * scl : -INFINITY;
-      float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m, mt);
-      const float alpha = fast_exp2(m - m_new);
-      float pr[4];
+    for (int i = 0; i < 4; ++i) s[i] = (key0 + i < ctx) ? s4[i] * scl : -INFINITY;
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mt = max_xor16(mt);
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m, mt);
+    const float alpha = fast_exp2(m - m_new);
+    float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
-      l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      m = m_new;
-      u32x2 pp;
-      pp.x = pack_bf16x2(pr[0] * vscl, pr[1] * vscl);
-      pp.y = pack_bf16x2(pr[2] * vscl, pr[3] * vscl);
-      const bf16x4 pf = __builtin_bit_cast(bf16x4, pp);
-      if (p * kPage + kPage > ctx) {
-        // Last, partly filled page: slots past the context hold unspecified
-        // bytes (possibly NaN); replace them so that 0 * NaN cannot occur.
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          u32x2 w = __builtin_bit_cast(u32x2, cur.v[db]);
-          if (key0 + 0 >= ctx) w.x &= 0xffff0000u;
-          if (key0 + 1 >= ctx) w.x &= 0x0000ffffu;
-          if (key0 + 2 >= ctx) w.y &= 0xffff0000u;
-          if (key0 + 3 >= ctx) w.y &= 0x0000ffffu;
-          cur.v[db] = __builtin_bit_cast(bf16x4, w);
-        }
-      }
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
+    l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    m = m_new;
+    u32x2 pp;
+    pp.x = pack_bf16x2(pr[0] * vscl, pr[1] * vscl);
+    pp.y = pack_bf16x2(pr[2] * vscl, pr[3] * vscl);
+    const bf16x4 pf = __builtin_bit_cast(bf16x4, pp);
+    if (p * kPage + kPage > ctx) {
+      // Last, partly filled page: slots past the context hold unspecified
+      // bytes (possibly NaN); replace them so that 0 * NaN cannot occur.
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        acc[db] *= alpha;
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(i16x4, cur.v[db]), __builtin_bit_cast(i16x4, pf), acc[db], 0,
-            0, 0);
+        u32x2 w = __builtin_bit_cast(u32x2, f.v[db]);
+        if (key0 + 0 >= ctx) w.x &= 0xffff0000u;
+        if (key0 + 1 >= ctx) w.x &= 0x0000ffffu;
+        if (key0 + 2 >= ctx) w.y &= 0xffff0000u;
+        if (key0 + 3 >= ctx) w.y &= 0x0000ffffu;
+        f.v[db] = __builtin_bit_cast(bf16x4, w);
       }
     }
-    cur = nxt;
-    phys = phys_n;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      acc[db] *= alpha;
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(i16x4, f.v[db]), __builtin_bit_cast(i16x4, pf), acc[db], 0, 0, 0);
+    }
+  };
+
+  // This wave's pages are p_begin + wave + 4*i.  Their block ids are read up
+  // front, one per lane (64 at a time), and three pages are kept in flight in
+  // a register ring: while one is folded in, the next two are loading.
+  const int first = p_begin + wave;
+  const int n_mine = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
+  for (int i0 = 0; i0 < n_mine; i0 += 64) {
+    const int n = min(64, n_mine - i0);
+    const int32_t my_id = lane < n ? bt[first + kWaves * (i0 + lane)] : -1;
+    auto id_at = [&](int i) -> int32_t { return __builtin_amdgcn_readlane(my_id, i); };
+    auto safe = [&](int32_t phys) -> int32_t { return valid_block(phys, a.num_blocks) ? phys : 0; };
+    KVFrag<D> fa, fb, fc;
+    // Loads past the last page repeat the last one (harmless, never folded).
+    load_page<D, FP8>(fa, a, safe(id_at(0)), g, lane);
+    load_page<D, FP8>(fb, a, safe(id_at(min(1, n - 1))), g, lane);
+    load_page<D, FP8>(fc, a, safe(id_at(min(2, n - 1))), g, lane);
+    // The loads are unconditional (past the end they re-read the last page,
+    // which is then a cache hit) so the compiler can count the loads still
+    // in flight instead of draining them all at the loop head.
+    for (int i = 0; i < n; i += 3) {
+      const int pa_ = first + kWaves * (i0 + i);
+      process(fa, pa_, valid_block(id_at(i), a.num_blocks));
+      load_page<D, FP8>(fa, a, safe(id_at(min(i + 3, n - 1))), g, lane);
+      process(fb, pa_ + kWaves, i + 1 < n && valid_block(id_at(min(i + 1, n - 1)), a.num_blocks));
+      load_page<D, FP8>(fb, a, safe(id_at(min(i + 4, n - 1))), g, lane);
+      process(fc, pa_ + 2 * kWaves,
+              i + 2 < n && valid_block(id_at(min(i + 2, n - 1)), a.num_blocks));
+      load_page<D, FP8>(fc, a, safe(id_at(min(i + 5, n - 1))), g, lane);
+    }
   }
 
   // Row sums: each lane group holds a quarter of the keys of head c.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum_xor16(l);
+  l = sum_xor32(l);
 
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
   __shared__ float sm_o[kWaves][D][17];

@@ -52,12 +52,28 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// The value held by lane l ^ 32 (v_permlane32_swap, no LDS round trip).
-__device__ __forceinline__ float swap_halves(float x) {
+// Symmetric pairwise combine of lane l with lane l ^ 32 / l ^ 16 through
+// v_permlane32_swap / v_permlane16_swap (no LDS round trip): with both
+// operands equal to x, the two results hold x[l] and x[l ^ k] in some order.
+__device__ __forceinline__ float max_xor32(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  // lanes 0-31 find their partner in the second result, lanes 32-63 in the first
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ----------------------------------------------------------------- launchers

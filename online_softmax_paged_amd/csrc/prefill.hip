@@ -175,7 +175,7 @@ __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(AttnArgs a, int n_tiles) {
   __shared__ Smem<D> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sv[i]), sv[i + 1]);
     mt = fmaxf(mt, sv[15]);
-    mt = fmaxf(mt, swap_halves(mt));
+    mt = max_xor32(mt);
     const float mt_s = mt * sc;  // scaled, log2 domain (sc > 0 keeps -inf)
     // Lazy rescaling: the running max (and with it O and l) is only moved when
     // some row's tile max exceeds it by more than 8, so exponents stay <= 2^8
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a, int n_tiles) {
     nxt = nn;
   }
 
-  l += swap_halves(l);
+  l = sum_xor32(l);
   if (!row_ok) return;
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
