@@ -108,11 +108,52 @@ __device__ __forceinline__ uint32_t zero_lo_hi(uint32_t w, bool lo_dead, bool hi
   return w;
 }
 
+// Register -> LDS without any masking (tile fully inside the context).
+template <int D, bool FP8>
+__device__ __forceinline__ void stage_store_plain(const Stage<D, FP8>& st, Smem<D>& sm, int buf,
+                                                  int tid) {
+  constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
+  constexpr int CPP = Stage<D, FP8>::CPP;
+#pragma unroll
+  for (int r = 0; r < Stage<D, FP8>::KCH; ++r) {
+    const int e = r * 256 + tid;
+    if (e >= 2 * CPP) break;
+    const int pg = e / CPP, within = e % CPP;
+    if constexpr (!FP8) {
+      const int tk = within / (D / 8), dc = within % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(pg * kPage + tk) * KS + dc * 8]) = st.k[r];
+      const int d = within >> 1, hf = within & 1;
+      uint16_t* dst = &sm.vt[buf][d * VS + pg * kPage + hf * 8];
+      *reinterpret_cast<u32x2*>(dst) = u32x2{st.v[r].x, st.v[r].y};
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{st.v[r].z, st.v[r].w};
+    } else {
+      const int tk = within / (D / 16), dc = within % (D / 16);
+      const u32x4 kw = st.k[r];
+      const u32x2 k0 = fp8x4_to_bf16x4(kw.x), k1 = fp8x4_to_bf16x4(kw.y);
+      const u32x2 k2 = fp8x4_to_bf16x4(kw.z), k3 = fp8x4_to_bf16x4(kw.w);
+      uint16_t* kd = &sm.k[buf][(pg * kPage + tk) * KS + dc * 16];
+      *reinterpret_cast<u32x4*>(kd) = u32x4{k0.x, k0.y, k1.x, k1.y};
+      *reinterpret_cast<u32x4*>(kd + 8) = u32x4{k2.x, k2.y, k3.x, k3.y};
+      const u32x4 vw = st.v[r];
+      uint16_t* vd = &sm.vt[buf][within * VS + pg * kPage];
+      *reinterpret_cast<u32x2*>(vd) = fp8x4_to_bf16x4(vw.x);
+      *reinterpret_cast<u32x2*>(vd + 4) = fp8x4_to_bf16x4(vw.y);
+      *reinterpret_cast<u32x2*>(vd + 8) = fp8x4_to_bf16x4(vw.z);
+      *reinterpret_cast<u32x2*>(vd + 12) = fp8x4_to_bf16x4(vw.w);
+    }
+  }
+}
+
 // Register -> LDS.  Slots at or past the context end are written as zeros so
 // that unspecified pool bytes (possibly NaN) never meet a zero probability.
 template <int D, bool FP8>
 __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm, int buf, int kt,
                                             int ctx, const TilePages& tp, int tid) {
+  // Common case: both pages are whole and inside the context; no masking.
+  if (tp.ok[0] && tp.ok[1] && (kt + 1) * kKeys <= ctx) {
+    stage_store_plain<D, FP8>(st, sm, buf, tid);
+    return;
+  }
   constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
   constexpr int CPP = Stage<D, FP8>::CPP;
 #pragma unroll
@@ -248,9 +289,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     bf16x8 kf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
+#ifdef PA_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+#ifdef PA_SETPRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
     // Score value i of this lane is key 8*(i/4) + 4*half + i%4 of the tile.
     // Raw scores (fp8: times the page's K scale); invisible keys -> -inf.
     float sv[16];
@@ -314,6 +361,294 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     __syncthreads();
     cur = nxt;
     nxt = nn;
+  }
+
+  l = sum_xor32(l);
+  if (!row_ok) return;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + qrow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w.x = pack_bf16x2(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv);
+      w.y = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + db * 32 + 8 * j + 4 * half) = w;
+    }
+  if (half == 0 && a.lse) a.lse[qrow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined variant: K tiles are staged one tile ahead of V tiles, so
+// in iteration kt a wave issues the score MFMAs of tile kt+1 in the same basic
+// block as the exponentials of tile kt; the matrix core and the vector ALU
+// then work at the same time inside one wave.
+
+template <int D, bool FP8>
+struct Half {  // staging of one operand (K or V) of one 32-key tile
+  static constexpr int CPP = FP8 ? kPage * D / 16 : kPage * D / 8;
+  static constexpr int KCH = (2 * CPP + 255) / 256;
+  u32x4 c[KCH];
+};
+
+template <int D, bool FP8, bool IS_V>
+__device__ __forceinline__ void half_load(Half<D, FP8>& h, const AttnArgs& a, int g,
+                                          const TilePages& tp, int tid) {
+  constexpr int CPP = Half<D, FP8>::CPP;
+  constexpr int ES = FP8 ? 16 : 8;
+#pragma unroll
+  for (int r = 0; r < Half<D, FP8>::KCH; ++r) {
+    const int e = min(r * 256 + tid, 2 * CPP - 1);
+    const int pg = e / CPP, within = e % CPP;
+    const bool ok = pg ? tp.ok[1] : tp.ok[0];
+    const int32_t phys = ok ? (pg ? tp.phys[1] : tp.phys[0]) : 0;
+    const int64_t base = (static_cast<int64_t>(phys) * a.num_kv_heads + g) * (kPage * D);
+    const void* src = IS_V ? a.v : a.k;
+    if constexpr (FP8)
+      h.c[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(src) + base + within * ES);
+    else
+      h.c[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + base + within * ES);
+  }
+}
+
+// Store one staged K tile (tile index kt) to LDS; masked only when the tile
+// is not entirely inside the context.
+template <int D, bool FP8>
+__device__ __forceinline__ void k_store(const Half<D, FP8>& h, uint16_t* kbuf, int kt, int ctx,
+                                        const TilePages& tp, int tid) {
+  constexpr int KS = Smem<D>::KS;
+  constexpr int CPP = Half<D, FP8>::CPP;
+  const bool plain = tp.ok[0] && tp.ok[1] && (kt + 1) * kKeys <= ctx;
+#pragma unroll
+  for (int r = 0; r < Half<D, FP8>::KCH; ++r) {
+    const int e = r * 256 + tid;
+    if (e >= 2 * CPP) break;
+    const int pg = e / CPP, within = e % CPP;
+    const int page_tok = (pg ? tp.ok[1] : tp.ok[0]) ? kt * kKeys + pg * kPage : ctx;
+    if constexpr (!FP8) {
+      const int tk = within / (D / 8), dc = within % (D / 8);
+      u32x4 kv = h.c[r];
+      if (!plain && page_tok + tk >= ctx) kv = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(&kbuf[(pg * kPage + tk) * KS + dc * 8]) = kv;
+    } else {
+      const int tk = within / (D / 16), dc = within % (D / 16);
+      const u32x4 kw = h.c[r];
+      const u32x2 k0 = fp8x4_to_bf16x4(kw.x), k1 = fp8x4_to_bf16x4(kw.y);
+      const u32x2 k2 = fp8x4_to_bf16x4(kw.z), k3 = fp8x4_to_bf16x4(kw.w);
+      u32x4 ka = {k0.x, k0.y, k1.x, k1.y}, kb = {k2.x, k2.y, k3.x, k3.y};
+      if (!plain && page_tok + tk >= ctx) ka = kb = u32x4{0, 0, 0, 0};
+      uint16_t* kd = &kbuf[(pg * kPage + tk) * KS + dc * 16];
+      *reinterpret_cast<u32x4*>(kd) = ka;
+      *reinterpret_cast<u32x4*>(kd + 8) = kb;
+    }
+  }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void v_store(const Half<D, FP8>& h, uint16_t* vbuf, int kt, int ctx,
+                                        const TilePages& tp, int tid) {
+  constexpr int VS = Smem<D>::VS;
+  constexpr int CPP = Half<D, FP8>::CPP;
+  const bool plain = tp.ok[0] && tp.ok[1] && (kt + 1) * kKeys <= ctx;
+#pragma unroll
+  for (int r = 0; r < Half<D, FP8>::KCH; ++r) {
+    const int e = r * 256 + tid;
+    if (e >= 2 * CPP) break;
+    const int pg = e / CPP, within = e % CPP;
+    const int page_tok = (pg ? tp.ok[1] : tp.ok[0]) ? kt * kKeys + pg * kPage : ctx;
+    if constexpr (!FP8) {
+      const int d = within >> 1, hf = within & 1;
+      const int t0 = page_tok + hf * 8;
+      u32x4 vv = h.c[r];
+      if (!plain && t0 + 8 > ctx) {
+        vv.x = zero_lo_hi(vv.x, t0 + 0 >= ctx, t0 + 1 >= ctx);
+        vv.y = zero_lo_hi(vv.y, t0 + 2 >= ctx, t0 + 3 >= ctx);
+        vv.z = zero_lo_hi(vv.z, t0 + 4 >= ctx, t0 + 5 >= ctx);
+        vv.w = zero_lo_hi(vv.w, t0 + 6 >= ctx, t0 + 7 >= ctx);
+      }
+      uint16_t* dst = &vbuf[d * VS + pg * kPage + hf * 8];
+      *reinterpret_cast<u32x2*>(dst) = u32x2{vv.x, vv.y};
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{vv.z, vv.w};
+    } else {
+      const u32x4 vw = h.c[r];
+      u32x2 w[4] = {fp8x4_to_bf16x4(vw.x), fp8x4_to_bf16x4(vw.y), fp8x4_to_bf16x4(vw.z),
+                    fp8x4_to_bf16x4(vw.w)};
+      if (!plain && page_tok + kPage > ctx) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[j].x = zero_lo_hi(w[j].x, page_tok + 4 * j + 0 >= ctx, page_tok + 4 * j + 1 >= ctx);
+          w[j].y = zero_lo_hi(w[j].y, page_tok + 4 * j + 2 >= ctx, page_tok + 4 * j + 3 >= ctx);
+        }
+      }
+      uint16_t* vd = &vbuf[within * VS + pg * kPage];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(vd + 4 * j) = w[j];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 scores(const uint16_t* kbuf, const bf16x8* qf, int col, int half) {
+  constexpr int KS = Smem<D>::KS;
+  const uint16_t* kb = &kbuf[col * KS + half * 8];
+  bf16x8 kf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
+  f32x16 s = {};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+  return s;
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_tiles) {
+  __shared__ Smem<D> sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y);
+  const int TQ = kRows / G;
+
+  const int q0 = a.cu_q_lens[b];
+  const int qlen = a.cu_q_lens[b + 1] - q0;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  const int t0 = tile * TQ;
+  if (t0 >= qlen) return;
+  const int pos_base = ctx - qlen;
+  const int t_last = min(t0 + TQ, qlen) - 1;
+  const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
+  if (kmax <= 0) return;
+  const int n_kt = (kmax + kKeys - 1) / kKeys;
+  const int n_pages = (ctx + kPage - 1) / kPage;
+  const int first_pos = pos_base + t0;
+  const int n_full = a.causal ? max(0, min((first_pos + 1) / kKeys, ctx / kKeys))
+                              : ctx / kKeys;
+
+  const int r = wave * 32 + col;
+  const int tt = t0 + r / G, hg = r % G;
+  const bool row_ok = tt < qlen;
+  const int qpos = pos_base + tt;
+  const int key_lim = a.causal ? min(qpos, ctx - 1) : ctx - 1;
+  const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
+
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
+  }
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const float sc = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f, mu = 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  // Prologue: K_0, V_0 and K_1 into LDS, scores of tile 0.
+  TilePages t0p = pages_of<FP8>(a, bt, 0, n_pages);
+  TilePages t1p = pages_of<FP8>(a, bt, 1, n_pages);
+  TilePages t2p = pages_of<FP8>(a, bt, 2, n_pages);
+  {
+    Half<D, FP8> hk0, hv0, hk1;
+    half_load<D, FP8, false>(hk0, a, g, t0p, tid);
+    half_load<D, FP8, true>(hv0, a, g, t0p, tid);
+    half_load<D, FP8, false>(hk1, a, g, t1p, tid);
+    k_store<D, FP8>(hk0, sm.k[0], 0, ctx, t0p, tid);
+    v_store<D, FP8>(hv0, sm.vt[0], 0, ctx, t0p, tid);
+    k_store<D, FP8>(hk1, sm.k[1], 1, ctx, t1p, tid);
+  }
+  __syncthreads();
+  f32x16 s_cur = scores<D>(sm.k[0], qf, col, half);
+
+  constexpr int VS = Smem<D>::VS;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // global loads for K_{kt+2} and V_{kt+1}; block ids for tile kt+3
+    const TilePages t3p = pages_of<FP8>(a, bt, kt + 3, n_pages);
+    Half<D, FP8> hk, hv;
+    half_load<D, FP8, false>(hk, a, g, t2p, tid);
+    half_load<D, FP8, true>(hv, a, g, t1p, tid);
+
+    // softmax statistics of tile kt
+    float sv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = FP8 ? s_cur[i] * (i < 8 ? t0p.ks[0] : t0p.ks[1]) : s_cur[i];
+    if (kt >= n_full) {
+      const int lim = key_lim - kt * kKeys - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? sv[i] : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sv[i]), sv[i + 1]);
+    mt = fmaxf(mt, sv[15]);
+    mt = max_xor32(mt);
+    const float mt_s = mt * sc;
+    if (__any(mt_s > m + 8.f)) {
+      const float m_new = fmaxf(m, mt_s);
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      m = m_new;
+      mu = m == -INFINITY ? 0.f : m;
+    }
+
+    // scores of tile kt+1 (independent of the exponentials below).  Computed
+    // unconditionally so both stay in one basic block; after the last tile the
+    // buffer holds finite stale keys and the result is discarded.
+    const f32x16 s_next = scores<D>(sm.k[(kt + 1) & 1], qf, col, half);
+
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -mu));
+      psum += sv[i];
+    }
+    l += psum;
+
+    // O^T += V^T . P^T for tile kt
+    const uint16_t* vbuf = sm.vt[kt & 1];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = FP8 ? sv[8 * c + i] * t0p.vs[c] : sv[8 * c + i];
+      u32x4 pw;
+      pw.x = pack_bf16x2(pv[0], pv[1]);
+      pw.y = pack_bf16x2(pv[2], pv[3]);
+      pw.z = pack_bf16x2(pv[4], pv[5]);
+      pw.w = pack_bf16x2(pv[6], pv[7]);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* vp = &vbuf[(db * 32 + col) * VS + c * kPage + half * 4];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+        const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
+                                                          acc[db], 0, 0, 0);
+      }
+    }
+    // K_{kt+2} replaces K_kt; V_{kt+1} replaces V_{kt-1}
+    if (kt + 2 < n_kt) k_store<D, FP8>(hk, sm.k[kt & 1], kt + 2, ctx, t2p, tid);
+    if (kt + 1 < n_kt) v_store<D, FP8>(hv, sm.vt[(kt + 1) & 1], kt + 1, ctx, t1p, tid);
+    __syncthreads();
+    s_cur = s_next;
+    t0p = t1p;
+    t1p = t2p;
+    t2p = t3p;
   }
 
   l = sum_xor32(l);
@@ -397,10 +732,17 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
   const int TQ = kRows / G;
   const int n_tiles = (a.max_q_len + TQ - 1) / TQ;
   const dim3 grid(a.num_seqs * a.num_kv_heads, n_tiles);
+#ifdef PA_PIPE
+  if (a.kv_dtype == PA_FP8_E4M3)
+    prefill_pipe_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
+  else
+    prefill_pipe_kernel<D, false><<<grid, 256, 0, st>>>(a, n_tiles);
+#else
   if (a.kv_dtype == PA_FP8_E4M3)
     prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
   else
     prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, n_tiles);
+#endif
   return hipGetLastError();
 }
 
