@@ -119,6 +119,11 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--decode-splits", type=int, default=0,
+                    help="KV splits for decode calls (0 = the library's choice)")
+    ap.add_argument("--flush-mb", type=int, default=-1,
+                    help="MB of scratch written between steps to evict the 256 MB last-level "
+                         "cache (-1 = 512 when a decode call reads less than 512 MB of KV)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -153,12 +158,17 @@ def main():
                                  max_ctx_len=mc, out=o, lse=lse))
             else:
                 B, Hq, D = q.shape
-                S = pa.decode_num_splits(B, wl.num_kv_heads, mc)
+                S = args.decode_splits or pa.decode_num_splits(B, wl.num_kv_heads, mc)
                 ws = torch.empty(max(1, pa.decode_workspace_bytes(B, Hq, D, S)), dtype=torch.uint8, device=dev)
                 fn = (lambda pool=pool, q=q, ctx=ctx, bt=bt, mc=mc, o=o, lse=lse, wl=wl, ws=ws, S=S:
                       pa.decode(pool, q, ctx, bt, wl.scale, max_ctx_len=mc, num_splits=S,
                                 workspace=ws, out=o, lse=lse))
             launches.append((call.kind, wl, call, fn))
+    flush_mb = args.flush_mb
+    if flush_mb < 0:
+        small = any(k == "decode" and decode_kv_bytes(c, w) < 512e6 for k, w, c, _ in launches)
+        flush_mb = 512 if small else 0
+    scratch = torch.ones(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -171,16 +181,22 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if scratch is not None:
+            # read (not write) the scratch: evicts the KV from the cache without
+            # leaving dirty lines whose write-back would overlap the timed launches
+            scratch.sum(dtype=torch.int64)
         for i, (_, _, _, fn) in enumerate(launches):
             evs[s][i][0].record()
             fn()
             evs[s][i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
 
     per_launch_ms = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)) / args.steps
                      for i in range(len(launches))]
+    # with a flush between steps the step time is the sum of the launches'
+    # event times; otherwise it is the wall clock of the K steps
+    ms_per_step = sum(per_launch_ms) if scratch is not None else wall * 1e3 / args.steps
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)"}
@@ -213,7 +229,7 @@ def main():
         result["unit"] = "GB/s"
     result["dtype"] = "bf16" if all(w.kv_dtype == "bf16" for w in wls) else \
         "+".join(sorted({("bf16-q/fp8-kv" if w.kv_dtype == "fp8" else w.kv_dtype) for w in wls}))
-    result["config"] = {"workload": " + ".join(w.name for w in wls)}
+    result["config"] = {"workload": " + ".join(w.name for w in wls), "cache_flush_mb": flush_mb}
     if pre:
         p = pre[0]
         result["roofline"] = {"bound": "mfma", "achieved": p["tflops"], "peak": PEAK_BF16_TFLOPS,

@@ -32,9 +32,11 @@
  *  - Metadata that lives on the device (lengths, block tables, slot mappings)
  *    is not read by the host.  The caller guarantees: 1 <= q_len_b <= ctx_len_b
  *    <= max_ctx_len, q_len_b <= max_q_len, and block_table[b][j] in
- *    [0, num_blocks) for every j < ceil(ctx_len_b / 16).  Entries past that are
- *    never read.  A block id outside [0, num_blocks) is never dereferenced (the
- *    page is treated as empty), but the result is then unspecified.
+ *    [0, num_blocks) for every j < ceil(ctx_len_b / 16).  Entries past that,
+ *    up to ceil(max_ctx_len / 16), may be read but their values are never used;
+ *    so bt_stride >= ceil(max_ctx_len / 16) (checked).  A block id outside
+ *    [0, num_blocks) is never dereferenced (the page is treated as empty), but
+ *    the result is then unspecified.
  *  - Calls are reentrant; the library keeps no mutable global state.
  */
 #ifndef PA_H

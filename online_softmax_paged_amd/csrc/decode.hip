@@ -39,40 +39,51 @@ struct KVFrag {
   float ks, vs;      // fp8 page scales
 };
 
-template <int D, bool FP8>
+// Load one page's K and V operands for this lane.  phys outside
+// [0, num_blocks) gives a zero-length buffer: the loads return zeros and read
+// nothing, so callers can issue them unconditionally.  NT selects streaming
+// (non-temporal) loads: right when the call reads far more K/V than the
+// last-level cache holds (measured ~7% more bandwidth), wrong when pages are
+// shared between sequences and could be served from cache.
+template <int D, bool FP8, bool NT>
 __device__ __forceinline__ void load_page(KVFrag<D>& f, const AttnArgs& a, int32_t phys, int g,
                                           int lane) {
-  const void* kbase = a.k;
-  const void* vbase = a.v;
-  const int64_t chunk = static_cast<int64_t>(phys) * a.num_kv_heads + g;
+  constexpr int kPol = NT ? kLoadNT : 0;
+  constexpr int ES = FP8 ? 1 : 2;
+  constexpr int BYTES = kPage * D * ES;
+  const bool ok = phys >= 0 && phys < a.num_blocks;
+  const int64_t chunk = ok ? static_cast<int64_t>(phys) * a.num_kv_heads + g : 0;
+  const auto rk = make_rsrc(static_cast<const char*>(a.k) + chunk * BYTES, ok ? BYTES : 0);
+  const auto rv = make_rsrc(static_cast<const char*>(a.v) + chunk * BYTES, ok ? BYTES : 0);
   const int c = lane & 15, grp = lane >> 4;
-  if constexpr (FP8) {
-    f.ks = a.k_scale[phys];
-    f.vs = a.v_scale[phys];
-  }
   if constexpr (!FP8) {
-    const uint16_t* kp = static_cast<const uint16_t*>(kbase) + chunk * (kPage * D);
-    const uint16_t* vp = static_cast<const uint16_t*>(vbase) + chunk * (kPage * D);
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      f.k[ks] = *reinterpret_cast<const bf16x8*>(kp + c * D + ks * 32 + grp * 8);
+      f.k[ks] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, (c * D + ks * 32 + grp * 8) * ES, 0,
+                                                        kPol));
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-      f.v[db] = *reinterpret_cast<const bf16x4*>(vp + (db * 16 + c) * kPage + grp * 4);
+      f.v[db] = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rv, ((db * 16 + c) * kPage + grp * 4) * ES,
+                                                       0, kPol));
   } else {
-    const uint8_t* kp = static_cast<const uint8_t*>(kbase) + chunk * (kPage * D);
-    const uint8_t* vp = static_cast<const uint8_t*>(vbase) + chunk * (kPage * D);
+    const auto rs = make_rsrc(a.k_scale, ok ? 4 * a.num_blocks : 0);
+    const auto rt = make_rsrc(a.v_scale, ok ? 4 * a.num_blocks : 0);
+    f.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? phys * 4 : 0, 0, 0));
+    f.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rt, ok ? phys * 4 : 0, 0, 0));
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(kp + c * D + ks * 32 + grp * 8);
+      const u32x2 w = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, c * D + ks * 32 + grp * 8, 0, kPol));
       const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
-      u32x4 r;
-      r.x = lo.x; r.y = lo.y; r.z = hi.x; r.w = hi.y;
-      f.k[ks] = __builtin_bit_cast(bf16x8, r);
+      f.k[ks] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + (db * 16 + c) * kPage + grp * 4);
+      const uint32_t w = __builtin_bit_cast(
+          uint32_t,
+          __builtin_amdgcn_raw_buffer_load_b32(rv, (db * 16 + c) * kPage + grp * 4, 0, kPol));
       f.v[db] = __builtin_bit_cast(bf16x4, fp8x4_to_bf16x4(w));
     }
   }
@@ -82,8 +93,13 @@ __device__ __forceinline__ bool valid_block(int32_t phys, int32_t nb) {
   return phys >= 0 && phys < nb;
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(256) void decode_split_kernel(AttnArgs a) {
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 2
+#endif
+
+template <int D, bool FP8, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
+void decode_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, grp = lane >> 4;
@@ -171,31 +187,34 @@ __global__ __launch_bounds__(256) void decode_split_kernel(AttnArgs a) {
 
   // This wave's pages are p_begin + wave + 4*i.  Their block ids are read up
   // front, one per lane (64 at a time), and three pages are kept in flight in
-  // a register ring: while one is folded in, the next two are loading.
+  // a register ring: while one is folded in, the next two are loading.  The
+  // ids are read for the split's whole range without waiting for the context
+  // length (entries past the sequence's last page are read, never used), and
+  // ring slots past the last page load from an empty buffer (no traffic), so
+  // every load is unconditional and the compiler can count those in flight.
   const int first = p_begin + wave;
+  const int range_end = min(p_begin + pps, max_pages);
+  const int n_spec = first < range_end ? (range_end - first + kWaves - 1) / kWaves : 0;
   const int n_mine = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
   for (int i0 = 0; i0 < n_mine; i0 += 64) {
     const int n = min(64, n_mine - i0);
-    const int32_t my_id = lane < n ? bt[first + kWaves * (i0 + lane)] : -1;
-    auto id_at = [&](int i) -> int32_t { return __builtin_amdgcn_readlane(my_id, i); };
-    auto safe = [&](int32_t phys) -> int32_t { return valid_block(phys, a.num_blocks) ? phys : 0; };
+    int32_t my_id = lane < min(64, n_spec - i0) ? bt[first + kWaves * (i0 + lane)] : -1;
+    my_id = lane < n ? my_id : -1;
+    auto id_at = [&](int i) -> int32_t {
+      return i < n ? __builtin_amdgcn_readlane(my_id, min(i, 63)) : -1;
+    };
     KVFrag<D> fa, fb, fc;
-    // Loads past the last page repeat the last one (harmless, never folded).
-    load_page<D, FP8>(fa, a, safe(id_at(0)), g, lane);
-    load_page<D, FP8>(fb, a, safe(id_at(min(1, n - 1))), g, lane);
-    load_page<D, FP8>(fc, a, safe(id_at(min(2, n - 1))), g, lane);
-    // The loads are unconditional (past the end they re-read the last page,
-    // which is then a cache hit) so the compiler can count the loads still
-    // in flight instead of draining them all at the loop head.
+    load_page<D, FP8, NT>(fa, a, id_at(0), g, lane);
+    load_page<D, FP8, NT>(fb, a, id_at(1), g, lane);
+    load_page<D, FP8, NT>(fc, a, id_at(2), g, lane);
     for (int i = 0; i < n; i += 3) {
       const int pa_ = first + kWaves * (i0 + i);
       process(fa, pa_, valid_block(id_at(i), a.num_blocks));
-      load_page<D, FP8>(fa, a, safe(id_at(min(i + 3, n - 1))), g, lane);
-      process(fb, pa_ + kWaves, i + 1 < n && valid_block(id_at(min(i + 1, n - 1)), a.num_blocks));
-      load_page<D, FP8>(fb, a, safe(id_at(min(i + 4, n - 1))), g, lane);
-      process(fc, pa_ + 2 * kWaves,
-              i + 2 < n && valid_block(id_at(min(i + 2, n - 1)), a.num_blocks));
-      load_page<D, FP8>(fc, a, safe(id_at(min(i + 5, n - 1))), g, lane);
+      load_page<D, FP8, NT>(fa, a, id_at(i + 3), g, lane);
+      process(fb, pa_ + kWaves, valid_block(id_at(i + 1), a.num_blocks));
+      load_page<D, FP8, NT>(fb, a, id_at(i + 4), g, lane);
+      process(fc, pa_ + 2 * kWaves, valid_block(id_at(i + 2), a.num_blocks));
+      load_page<D, FP8, NT>(fc, a, id_at(i + 5), g, lane);
     }
   }
 
@@ -387,10 +406,19 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
     decode_f32_kernel<D><<<grid, 256, 0, st>>>(a);
   } else {
     const dim3 grid(S, a.num_kv_heads, a.num_seqs);
-    if (a.kv_dtype == PA_FP8_E4M3)
-      decode_split_kernel<D, true><<<grid, 256, 0, st>>>(a);
-    else
-      decode_split_kernel<D, false><<<grid, 256, 0, st>>>(a);
+    // Stream (non-temporal loads) when the largest possible K/V read of the
+    // call is well beyond the 256 MB last-level cache.
+    const double es = a.kv_dtype == PA_FP8_E4M3 ? 1.0 : 2.0;
+    const double max_bytes =
+        2.0 * es * D * a.num_kv_heads * static_cast<double>(a.num_seqs) * a.max_ctx_len;
+    const bool nt = max_bytes > 512.0 * (1 << 20);
+    if (a.kv_dtype == PA_FP8_E4M3) {
+      if (nt) decode_split_kernel<D, true, true><<<grid, 256, 0, st>>>(a);
+      else decode_split_kernel<D, true, false><<<grid, 256, 0, st>>>(a);
+    } else {
+      if (nt) decode_split_kernel<D, false, true><<<grid, 256, 0, st>>>(a);
+      else decode_split_kernel<D, false, false><<<grid, 256, 0, st>>>(a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;

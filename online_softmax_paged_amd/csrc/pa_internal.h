@@ -19,6 +19,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
@@ -51,6 +52,16 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resources.  A buffer load whose byte offset is at or past
+// num_records returns zero without touching memory, so a descriptor with
+// num_records = 0 makes a "dummy" load that can stay unconditional.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format
+constexpr int kLoadNT = 2;              // non-temporal (streaming) cache policy
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           kRsrcWord3);
+}
 
 // Symmetric pairwise combine of lane l with lane l ^ 32 / l ^ 16 through
 // v_permlane32_swap / v_permlane16_swap (no LDS round trip): with both

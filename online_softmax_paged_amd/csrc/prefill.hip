@@ -289,15 +289,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     bf16x8 kf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
-#ifdef PA_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-#ifdef PA_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
     // Score value i of this lane is key 8*(i/4) + 4*half + i%4 of the tile.
     // Raw scores (fp8: times the page's K scale); invisible keys -> -inf.
     float sv[16];
@@ -381,138 +375,158 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined variant: K tiles are staged one tile ahead of V tiles, so
-// in iteration kt a wave issues the score MFMAs of tile kt+1 in the same basic
-// block as the exponentials of tile kt; the matrix core and the vector ALU
-// then work at the same time inside one wave.
+// bf16 pools: K/V tiles go from HBM straight into LDS (buffer loads with the
+// LDS modifier; each wave instruction fills 1 KiB = 64 lanes x 16 B), so the
+// staging needs no registers and no LDS store instructions.  Three LDS stages:
+// tile kt+2 is loading while tile kt is multiplied.
+//
+// LDS layouts (16-byte chunks, swizzled so the MFMA operand reads are free of
+// bank conflicts while each DMA instruction still writes 1 KiB contiguously):
+//   K   [32 keys][D/8 chunks]: logical chunk j of key row r sits at j ^ (r % (D/8)).
+//   V^T per page c: [D rows][2 chunks of 8 keys]: chunk e of row d sits at
+//       e ^ ((d / 8) % 2).
+// The P.V product reads V^T chunks of 8 consecutive keys (one ds_read_b128),
+// so the P operand is rearranged with two v_permlane32_swap per page to the
+// same key order.
+// Tail handling: pages outside the sequence and K rows past the context end
+// come from a shortened buffer range (zero-filled by the hardware); V^T slots
+// past the context end of the last page are zeroed in LDS before use.
 
-template <int D, bool FP8>
-struct Half {  // staging of one operand (K or V) of one 32-key tile
-  static constexpr int CPP = FP8 ? kPage * D / 16 : kPage * D / 8;
-  static constexpr int KCH = (2 * CPP + 255) / 256;
-  u32x4 c[KCH];
+// Block ids of one tile, read raw (clamped index, no checks) so nothing waits
+// on the load until the ids are used an iteration later.
+struct RawPages {
+  int32_t id[2];
 };
 
-template <int D, bool FP8, bool IS_V>
-__device__ __forceinline__ void half_load(Half<D, FP8>& h, const AttnArgs& a, int g,
-                                          const TilePages& tp, int tid) {
-  constexpr int CPP = Half<D, FP8>::CPP;
-  constexpr int ES = FP8 ? 16 : 8;
+__device__ __forceinline__ TilePages check_pages(const AttnArgs& a, const RawPages& r, int t,
+                                                 int n_pages) {
+  TilePages tp;
 #pragma unroll
-  for (int r = 0; r < Half<D, FP8>::KCH; ++r) {
-    const int e = min(r * 256 + tid, 2 * CPP - 1);
-    const int pg = e / CPP, within = e % CPP;
-    const bool ok = pg ? tp.ok[1] : tp.ok[0];
-    const int32_t phys = ok ? (pg ? tp.phys[1] : tp.phys[0]) : 0;
-    const int64_t base = (static_cast<int64_t>(phys) * a.num_kv_heads + g) * (kPage * D);
-    const void* src = IS_V ? a.v : a.k;
-    if constexpr (FP8)
-      h.c[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(src) + base + within * ES);
-    else
-      h.c[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + base + within * ES);
+  for (int j = 0; j < 2; ++j) {
+    const int32_t phys = 2 * t + j < n_pages ? r.id[j] : -1;
+    tp.phys[j] = phys;
+    tp.ok[j] = phys >= 0 && phys < a.num_blocks;
+    tp.ks[j] = tp.vs[j] = 1.f;
   }
-}
-
-// Store one staged K tile (tile index kt) to LDS; masked only when the tile
-// is not entirely inside the context.
-template <int D, bool FP8>
-__device__ __forceinline__ void k_store(const Half<D, FP8>& h, uint16_t* kbuf, int kt, int ctx,
-                                        const TilePages& tp, int tid) {
-  constexpr int KS = Smem<D>::KS;
-  constexpr int CPP = Half<D, FP8>::CPP;
-  const bool plain = tp.ok[0] && tp.ok[1] && (kt + 1) * kKeys <= ctx;
-#pragma unroll
-  for (int r = 0; r < Half<D, FP8>::KCH; ++r) {
-    const int e = r * 256 + tid;
-    if (e >= 2 * CPP) break;
-    const int pg = e / CPP, within = e % CPP;
-    const int page_tok = (pg ? tp.ok[1] : tp.ok[0]) ? kt * kKeys + pg * kPage : ctx;
-    if constexpr (!FP8) {
-      const int tk = within / (D / 8), dc = within % (D / 8);
-      u32x4 kv = h.c[r];
-      if (!plain && page_tok + tk >= ctx) kv = u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(&kbuf[(pg * kPage + tk) * KS + dc * 8]) = kv;
-    } else {
-      const int tk = within / (D / 16), dc = within % (D / 16);
-      const u32x4 kw = h.c[r];
-      const u32x2 k0 = fp8x4_to_bf16x4(kw.x), k1 = fp8x4_to_bf16x4(kw.y);
-      const u32x2 k2 = fp8x4_to_bf16x4(kw.z), k3 = fp8x4_to_bf16x4(kw.w);
-      u32x4 ka = {k0.x, k0.y, k1.x, k1.y}, kb = {k2.x, k2.y, k3.x, k3.y};
-      if (!plain && page_tok + tk >= ctx) ka = kb = u32x4{0, 0, 0, 0};
-      uint16_t* kd = &kbuf[(pg * kPage + tk) * KS + dc * 16];
-      *reinterpret_cast<u32x4*>(kd) = ka;
-      *reinterpret_cast<u32x4*>(kd + 8) = kb;
-    }
-  }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void v_store(const Half<D, FP8>& h, uint16_t* vbuf, int kt, int ctx,
-                                        const TilePages& tp, int tid) {
-  constexpr int VS = Smem<D>::VS;
-  constexpr int CPP = Half<D, FP8>::CPP;
-  const bool plain = tp.ok[0] && tp.ok[1] && (kt + 1) * kKeys <= ctx;
-#pragma unroll
-  for (int r = 0; r < Half<D, FP8>::KCH; ++r) {
-    const int e = r * 256 + tid;
-    if (e >= 2 * CPP) break;
-    const int pg = e / CPP, within = e % CPP;
-    const int page_tok = (pg ? tp.ok[1] : tp.ok[0]) ? kt * kKeys + pg * kPage : ctx;
-    if constexpr (!FP8) {
-      const int d = within >> 1, hf = within & 1;
-      const int t0 = page_tok + hf * 8;
-      u32x4 vv = h.c[r];
-      if (!plain && t0 + 8 > ctx) {
-        vv.x = zero_lo_hi(vv.x, t0 + 0 >= ctx, t0 + 1 >= ctx);
-        vv.y = zero_lo_hi(vv.y, t0 + 2 >= ctx, t0 + 3 >= ctx);
-        vv.z = zero_lo_hi(vv.z, t0 + 4 >= ctx, t0 + 5 >= ctx);
-        vv.w = zero_lo_hi(vv.w, t0 + 6 >= ctx, t0 + 7 >= ctx);
-      }
-      uint16_t* dst = &vbuf[d * VS + pg * kPage + hf * 8];
-      *reinterpret_cast<u32x2*>(dst) = u32x2{vv.x, vv.y};
-      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{vv.z, vv.w};
-    } else {
-      const u32x4 vw = h.c[r];
-      u32x2 w[4] = {fp8x4_to_bf16x4(vw.x), fp8x4_to_bf16x4(vw.y), fp8x4_to_bf16x4(vw.z),
-                    fp8x4_to_bf16x4(vw.w)};
-      if (!plain && page_tok + kPage > ctx) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          w[j].x = zero_lo_hi(w[j].x, page_tok + 4 * j + 0 >= ctx, page_tok + 4 * j + 1 >= ctx);
-          w[j].y = zero_lo_hi(w[j].y, page_tok + 4 * j + 2 >= ctx, page_tok + 4 * j + 3 >= ctx);
-        }
-      }
-      uint16_t* vd = &vbuf[within * VS + pg * kPage];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(vd + 4 * j) = w[j];
-    }
-  }
+  return tp;
 }
 
 template <int D>
-__device__ __forceinline__ f32x16 scores(const uint16_t* kbuf, const bf16x8* qf, int col, int half) {
-  constexpr int KS = Smem<D>::KS;
-  const uint16_t* kb = &kbuf[col * KS + half * 8];
-  bf16x8 kf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kb + ks * 16);
-  f32x16 s = {};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-  return s;
+struct DmaSmem {
+  static constexpr int KB = kKeys * D * 2;      // K tile bytes
+  static constexpr int VB = kKeys * D * 2;      // V^T tile bytes (2 pages)
+  static constexpr int STAGE = KB + VB;
+  char buf[3 * STAGE];
+};
+
+// One buffer load of 16 bytes per lane straight into LDS: lane i's bytes
+// [voffset, voffset + 16) of the buffer [base, base + nbytes) land at
+// lds_addr + 16 * i; bytes at or past nbytes read as zero.  Written as inline
+// asm so the compiler's wait-count pass does not drain all outstanding loads
+// before each write of M0 (the hardware latches M0 when the load issues);
+// callers wait with wait_vmcnt<>() before the data is used.  The instruction
+// writes no register, and s_nop covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void dma16(const void* base, int32_t nbytes, uint32_t voffset,
+                                      const void* lds) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))),
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffff)),
+                    __builtin_amdgcn_readfirstlane(nbytes), kRsrcWord3};
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds)));
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rs), "{m0}"(m0)
+               : "memory");
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_tiles) {
-  __shared__ Smem<D> sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// Instruction u (0 .. D/8 - 1) of a tile is issued by wave u % NW: the first
+// D/16 move K (1 KiB each), the rest move V^T.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(const AttnArgs& a, int g, const TilePages& tp, int t,
+                                         int ctx, char* stage, int wave, int lane) {
+  constexpr int CPR = D / 8;            // 16-byte chunks per K row
+  constexpr int NK = D / 16;            // K instructions per tile (= V instructions)
+  constexpr int PAGE_BYTES = kPage * D * 2;
+#pragma unroll
+  for (int u0 = 0; u0 < 2 * NK; u0 += NW) {
+    const int u = u0 + wave;
+    if (u >= 2 * NK) break;
+    if (u < NK) {
+      // --- K: LDS chunk m = u*64 + lane -> (row r, position p)
+      const int m = u * 64 + lane;
+      const int r = m / CPR, pos = m % CPR;
+      const int logical = pos ^ (r % CPR);
+      const bool pg = (u * 64 / CPR) / kPage;  // uniform per instruction
+      const int tok = r % kPage;
+      const int page_tok0 = t * kKeys + (pg ? kPage : 0);
+      const bool ok = pg ? tp.ok[1] : tp.ok[0];
+      const int n_valid = ok ? max(0, min(kPage, ctx - page_tok0)) : 0;
+      const int64_t chunk =
+          ok ? static_cast<int64_t>(pg ? tp.phys[1] : tp.phys[0]) * a.num_kv_heads + g : 0;
+      dma16(static_cast<const char*>(a.k) + chunk * PAGE_BYTES, n_valid * D * 2,
+            (tok * CPR + logical) * 16, stage + u * 1024);
+    } else {
+      // --- V^T: LDS chunk m = (u-NK)*64 + lane -> page, row d, position e'
+      const int uv = u - NK;
+      const int m = uv * 64 + lane;
+      const bool pg = (uv * 64) / (2 * D);     // uniform per instruction
+      const int mm = m % (2 * D);
+      const int d = mm >> 1, ep = mm & 1;
+      const int e = ep ^ ((d >> 3) & 1);
+      const int page_tok0 = t * kKeys + (pg ? kPage : 0);
+      const bool ok = (pg ? tp.ok[1] : tp.ok[0]) && page_tok0 < ctx;
+      const int64_t chunk =
+          ok ? static_cast<int64_t>(pg ? tp.phys[1] : tp.phys[0]) * a.num_kv_heads + g : 0;
+      dma16(static_cast<const char*>(a.v) + chunk * PAGE_BYTES, ok ? PAGE_BYTES : 0,
+            (d * 2 + e) * 16, stage + DmaSmem<D>::KB + uv * 1024);
+    }
+  }
+}
+
+// Wait until at most n of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Same, for a wave-uniform count known only at run time (0..4).
+__device__ __forceinline__ void wait_vmcnt_upto4(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    default: wait_vmcnt<4>(); break;
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW >= 8 ? 2 : 3)))
+void prefill_dma_kernel(AttnArgs a, int n_tiles) {
+  __shared__ DmaSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-  const int bg = blockIdx.x;
+  // Workgroups are dealt to the 8 dies (XCDs, each with its own L2) round
+  // robin by linear id.  Remap so die k runs a contiguous range of tasks
+  // ordered (sequence x KV head)-major, query tiles longest first: a die then
+  // streams about one (sequence, KV head)'s K/V at a time, which fits its L2.
+  const int n_bg = gridDim.x;
+  const int n_tasks = n_bg * n_tiles;
+  const int lin = blockIdx.y * n_bg + blockIdx.x;
+  const int task = (n_tasks % 8 == 0) ? (lin % 8) * (n_tasks / 8) + lin / 8 : lin;
+  const int bg = (n_tasks % 8 == 0) ? task / n_tiles : blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y);
-  const int TQ = kRows / G;
+  const int tile = n_tiles - 1 - ((n_tasks % 8 == 0) ? task % n_tiles : static_cast<int>(blockIdx.y));
+  constexpr int ROWS = 32 * NW;   // query rows per workgroup
+  const int TQ = ROWS / G;
+  constexpr int STAGE = DmaSmem<D>::STAGE;
+  constexpr int CPR = D / 8;
+  // DMA instructions this wave issues per tile
+  const int my_dma = (D / 8 - wave + NW - 1) / NW;
 
   const int q0 = a.cu_q_lens[b];
   const int qlen = a.cu_q_lens[b + 1] - q0;
@@ -529,6 +543,8 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_til
   const int first_pos = pos_base + t0;
   const int n_full = a.causal ? max(0, min((first_pos + 1) / kKeys, ctx / kKeys))
                               : ctx / kKeys;
+  // the tile holding the context end, if that end is not on a page boundary
+  const int tail_tile = (ctx % kPage) ? (ctx - 1) / kKeys : -1;
 
   const int r = wave * 32 + col;
   const int tt = t0 + r / G, hg = r % G;
@@ -536,6 +552,27 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_til
   const int qpos = pos_base + tt;
   const int key_lim = a.causal ? min(qpos, ctx - 1) : ctx - 1;
   const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  // Block ids of 64 consecutive pages, one per lane, refreshed every 32
+  // tiles; a tile's two ids are then register reads, not memory loads.
+  int id_chunk = 0;
+  int32_t idv = lane < n_pages ? bt[lane] : -1;
+  auto tile_pages = [&](int t) -> TilePages {
+    const int c = (2 * t) >> 6;
+    if (c != id_chunk) {  // uniform; at most once per 32 tiles
+      id_chunk = c;
+      idv = 64 * c + lane < n_pages ? bt[64 * c + lane] : -1;
+      // consume the load here, so its wait stays inside this rare branch
+      asm volatile("" ::"v"(idv));
+    }
+    RawPages r;
+    r.id[0] = __builtin_amdgcn_readlane(idv, (2 * t) & 63);
+    r.id[1] = __builtin_amdgcn_readlane(idv, (2 * t + 1) & 63);
+    return check_pages(a, r, t, n_pages);
+  };
+  dma_tile<D, NW>(a, g, tile_pages(0), 0, ctx, sm.buf, wave, lane);
+  dma_tile<D, NW>(a, g, tile_pages(1), 1, ctx, sm.buf + STAGE, wave, lane);
 
   bf16x8 qf[D / 16];
   {
@@ -546,8 +583,6 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_til
       qf[ks] = row_ok ? v : bf16x8{};
     }
   }
-
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
   const float sc = a.scale * kLog2e;
   float m = -INFINITY, l = 0.f, mu = 0.f;
   f32x16 acc[D / 32];
@@ -556,34 +591,45 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_til
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  // Prologue: K_0, V_0 and K_1 into LDS, scores of tile 0.
-  TilePages t0p = pages_of<FP8>(a, bt, 0, n_pages);
-  TilePages t1p = pages_of<FP8>(a, bt, 1, n_pages);
-  TilePages t2p = pages_of<FP8>(a, bt, 2, n_pages);
-  {
-    Half<D, FP8> hk0, hv0, hk1;
-    half_load<D, FP8, false>(hk0, a, g, t0p, tid);
-    half_load<D, FP8, true>(hv0, a, g, t0p, tid);
-    half_load<D, FP8, false>(hk1, a, g, t1p, tid);
-    k_store<D, FP8>(hk0, sm.k[0], 0, ctx, t0p, tid);
-    v_store<D, FP8>(hv0, sm.vt[0], 0, ctx, t0p, tid);
-    k_store<D, FP8>(hk1, sm.k[1], 1, ctx, t1p, tid);
-  }
+  wait_vmcnt_upto4(my_dma);  // tile 0 landed (tile 1 may still be in flight)
   __syncthreads();
-  f32x16 s_cur = scores<D>(sm.k[0], qf, col, half);
 
-  constexpr int VS = Smem<D>::VS;
   for (int kt = 0; kt < n_kt; ++kt) {
-    // global loads for K_{kt+2} and V_{kt+1}; block ids for tile kt+3
-    const TilePages t3p = pages_of<FP8>(a, bt, kt + 3, n_pages);
-    Half<D, FP8> hk, hv;
-    half_load<D, FP8, false>(hk, a, g, t2p, tid);
-    half_load<D, FP8, true>(hv, a, g, t1p, tid);
+    char* stg = sm.buf + (kt % 3) * STAGE;
+    if (kt == tail_tile) {
+      // zero V^T slots of tokens at or past the context end in this stage
+      uint16_t* vt = reinterpret_cast<uint16_t*>(stg + DmaSmem<D>::KB);
+      for (int e = tid; e < 2 * D * kPage; e += 64 * NW) {
+        const int pg = e / (D * kPage), rem = e % (D * kPage);
+        const int d = rem / kPage, k = rem % kPage;
+        if (kt * kKeys + pg * kPage + k >= ctx) {
+          const int chunk = (k >> 3) ^ ((d >> 3) & 1);
+          vt[pg * D * kPage + d * kPage + chunk * 8 + (k & 7)] = 0;
+        }
+      }
+      __syncthreads();
+    }
+    // DMA tile kt+2 into the stage tile kt-1 used (all waves are past it)
+    if (kt + 2 < n_kt)
+      dma_tile<D, NW>(a, g, tile_pages(kt + 2), kt + 2, ctx, sm.buf + ((kt + 2) % 3) * STAGE,
+                      wave, lane);
 
-    // softmax statistics of tile kt
+    // S^T = K . Q^T
+    const char* kbase = stg + col * (D * 2);
+    bf16x8 kf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int logical = 2 * ks + half;
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + ((logical ^ (col % CPR)) * 16));
+    }
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+
     float sv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = FP8 ? s_cur[i] * (i < 8 ? t0p.ks[0] : t0p.ks[1]) : s_cur[i];
+    for (int i = 0; i < 16; ++i) sv[i] = s[i];
     if (kt >= n_full) {
       const int lim = key_lim - kt * kKeys - 4 * half;
 #pragma unroll
@@ -604,12 +650,6 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_til
       m = m_new;
       mu = m == -INFINITY ? 0.f : m;
     }
-
-    // scores of tile kt+1 (independent of the exponentials below).  Computed
-    // unconditionally so both stay in one basic block; after the last tile the
-    // buffer holds finite stale keys and the result is discarded.
-    const f32x16 s_next = scores<D>(sm.k[(kt + 1) & 1], qf, col, half);
-
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -618,37 +658,30 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(AttnArgs a, int n_til
     }
     l += psum;
 
-    // O^T += V^T . P^T for tile kt
-    const uint16_t* vbuf = sm.vt[kt & 1];
+    // O^T += V^T . P^T, page c = keys 16c..16c+15 of the tile
+    const char* vbase = stg + DmaSmem<D>::KB;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = FP8 ? sv[8 * c + i] * t0p.vs[c] : sv[8 * c + i];
-      u32x4 pw;
-      pw.x = pack_bf16x2(pv[0], pv[1]);
-      pw.y = pack_bf16x2(pv[2], pv[3]);
-      pw.z = pack_bf16x2(pv[4], pv[5]);
-      pw.w = pack_bf16x2(pv[6], pv[7]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      // this lane holds keys 16c + 4*half + {0..3} (A) and 16c + 8 + 4*half + {0..3} (B);
+      // after the swaps: half 0 holds keys 16c + 0..7, half 1 holds 16c + 8..15
+      uint32_t A0 = pack_bf16x2(sv[8 * c + 0], sv[8 * c + 1]);
+      uint32_t A1 = pack_bf16x2(sv[8 * c + 2], sv[8 * c + 3]);
+      uint32_t B0 = pack_bf16x2(sv[8 * c + 4], sv[8 * c + 5]);
+      uint32_t B1 = pack_bf16x2(sv[8 * c + 6], sv[8 * c + 7]);
+      const auto r0 = __builtin_amdgcn_permlane32_swap(A0, B0, false, false);
+      const auto r1 = __builtin_amdgcn_permlane32_swap(A1, B1, false, false);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{r0[0], r1[0], r0[1], r1[1]});
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* vp = &vbuf[(db * 32 + col) * VS + c * kPage + half * 4];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-        const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
-                                                          acc[db], 0, 0, 0);
+        const int d = db * 32 + col;
+        const int ep = half ^ ((d >> 3) & 1);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vbase + c * (D * kPage * 2) + d * 32 + ep * 16);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
       }
     }
-    // K_{kt+2} replaces K_kt; V_{kt+1} replaces V_{kt-1}
-    if (kt + 2 < n_kt) k_store<D, FP8>(hk, sm.k[kt & 1], kt + 2, ctx, t2p, tid);
-    if (kt + 1 < n_kt) v_store<D, FP8>(hv, sm.vt[(kt + 1) & 1], kt + 1, ctx, t1p, tid);
+    // tile kt+1 must have landed before the barrier; tile kt+2 may still fly
+    if (kt + 2 < n_kt) wait_vmcnt_upto4(my_dma); else wait_vmcnt<0>();
     __syncthreads();
-    s_cur = s_next;
-    t0p = t1p;
-    t1p = t2p;
-    t2p = t3p;
   }
 
   l = sum_xor32(l);
@@ -729,20 +762,17 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int TQ = kRows / G;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+  constexpr int NW = PA_PREFILL_WAVES;
+  const int TQ = (a.kv_dtype == PA_BF16 ? 32 * NW : kRows) / G;
   const int n_tiles = (a.max_q_len + TQ - 1) / TQ;
   const dim3 grid(a.num_seqs * a.num_kv_heads, n_tiles);
-#ifdef PA_PIPE
-  if (a.kv_dtype == PA_FP8_E4M3)
-    prefill_pipe_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
-  else
-    prefill_pipe_kernel<D, false><<<grid, 256, 0, st>>>(a, n_tiles);
-#else
   if (a.kv_dtype == PA_FP8_E4M3)
     prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
   else
-    prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, n_tiles);
-#endif
+    prefill_dma_kernel<D, NW><<<grid, 64 * NW, 0, st>>>(a, n_tiles);
   return hipGetLastError();
 }
 

@@ -149,7 +149,7 @@ def test_decode_workspace_checks():
 
 def test_decode_split_heuristic():
     # long context, few sequences: many splits; short contexts: few
-    assert pa.decode_num_splits(8, 8, 32768) == 16
+    assert pa.decode_num_splits(8, 8, 32768) == 8
     assert pa.decode_num_splits(1, 1, 100) == 1
     assert 1 <= pa.decode_num_splits(32, 8, 2048) <= 16
     assert pa.decode_num_splits(0, 8, 100) == 1
