@@ -1,6 +1,7 @@
 """Benchmark of the paged attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload headline|1..5] [--no-cpu-baseline]
+    python bench.py --pmc-summary FETCH.csv WRITE.csv --copy-calib-mb N   (host only)
 
 One step runs every call of the selected workloads once, inputs already
 resident in HBM (the pool write is setup and is not timed).  The default
@@ -68,6 +69,66 @@ def traffic_for(kernel_file: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _pmc_per_dispatch(path: str):
+    """{kernel name: [counter value of each dispatch]} from one rocprofv3
+    counter_collection.csv holding a single counter."""
+    import collections
+    import csv
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in csv.DictReader(open(path)):
+        per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, copy_mb: int, names: dict):
+    """Turn a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch) into HBM
+    bytes per launch of each library kernel.  Each counter is scaled by the
+    ratio of the known size of a plain device-to-device copy of copy_mb MiB to
+    what the same counter read for it; the result is stored, with a hash of the
+    kernel source, in profiles/hbm_traffic.json."""
+    fetch, write = _pmc_per_dispatch(fetch_csv), _pmc_per_dispatch(write_csv)
+
+    def copy_kib(d):
+        # the calibration copy is by far the largest blit dispatch of the run
+        cands = [max(v) for k, v in d.items() if "copyBuffer" in k]
+        return max(cands) if cands else None
+
+    known_kib = float(copy_mb) * 1024
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    if not cf or not cw:
+        raise SystemExit("no copy kernel found in the counter files")
+    f_fetch, f_write = known_kib / cf, known_kib / cw
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    files = {"prefill_dma_kernel": "prefill.hip", "prefill_kernel": "prefill.hip",
+             "prefill_f32_kernel": "prefill.hip", "decode_split_kernel": "decode.hip",
+             "decode_f32_kernel": "decode.hip", "decode_merge_kernel": "decode.hip"}
+    rows = []
+    for name, fv in sorted(fetch.items()):
+        short = name.replace("pa::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        base = short.split("<")[0]
+        if base not in files or name not in write:
+            continue
+        n, fk = len(fv), sum(fv) / len(fv)
+        wk = sum(write[name]) / len(write[name])
+        by = (fk * f_fetch + wk * f_write) * 1024
+        rows.append((short, n, fk * f_fetch * 1024, wk * f_write * 1024, by))
+        workload = names["prefill" if base.startswith("prefill") else "decode"]
+        # the merge pass is keyed apart from the main kernel of its call
+        key = f"{files[base]}:{workload}" + (":merge" if base == "decode_merge_kernel" else "")
+        data[key] = {"kernel": short, "bytes_per_launch": by, "fetch_bytes": fk * f_fetch * 1024,
+                     "write_bytes": wk * f_write * 1024, "dispatches": n,
+                     "source_sha": _src_hash(files[base])}
+    data["_calibration"] = {"copy_mib": copy_mb, "fetch_factor": f_fetch, "write_factor": f_write}
+    json.dump(data, open(path, "w"), indent=1, sort_keys=True)
+    print(f"copy of {copy_mb} MiB: FETCH_SIZE x{f_fetch:.4f}, WRITE_SIZE x{f_write:.4f}")
+    print("| kernel | dispatches | HBM read MB | HBM write MB | total MB |")
+    print("|---|---|---|---|---|")
+    for short, n, fb, wb, by in rows:
+        print(f"| `{short}` | {n} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {by / 1e6:.1f} |")
+
+
 def cpu_baseline(wls, budget_s: float):
     """Time the float64 oracle on a bounded sample of the same workloads."""
     import numpy as np
@@ -124,7 +185,24 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="MB of scratch written between steps to evict the 256 MB last-level "
                          "cache (-1 = 512 when a decode call reads less than 512 MB of KV)")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB after the "
+                         "warmup (outside the timed region) to calibrate HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: summarise two rocprofv3 --pmc runs of this script "
+                         "(FETCH_SIZE, then WRITE_SIZE) into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.pmc_summary:
+        if not args.copy_calib_mb:
+            raise SystemExit("--pmc-summary needs the --copy-calib-mb the runs used")
+        import workloads
+        if args.workload == "headline":
+            names = {"prefill": workloads.NAMES[3], "decode": workloads.NAMES[4]}
+        else:
+            n = workloads.NAMES[int(args.workload)]
+            names = {"prefill": n, "decode": n}
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_calib_mb, names)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence and KV head, see the design notes).", file=sys.stderr)
@@ -175,6 +253,13 @@ def main():
         for _, _, _, fn in launches:
             fn()
     torch.cuda.synchronize()
+    if args.copy_calib_mb:
+        src = torch.ones(args.copy_calib_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in launches] for _ in range(args.steps)]

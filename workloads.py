@@ -163,10 +163,18 @@ def build(name: str, *, kv_dtype: str, q_dtype: str, num_q_heads: int,
 # ---------------------------------------------------------------------------
 # The five named workloads.  Seeds are 1000 + k for workload k.
 
+NAMES = {
+    1: "tiny_fp32_1x256_d64",
+    2: "decode_bf16_32seq_len128-2048_gqa4_d128",
+    3: "prefill_bf16_4x4096_gqa4_d128",
+    4: "decode_bf16_8x32768_gqa8_d128",
+    5: "mixed_fp8kv_16x1536_prefix1024_gqa4_d128",
+}
+
 def tiny_fp32() -> Workload:
     """1 sequence, 1 head, d=64, 256 tokens in 16 shuffled pages; causal
     prefill of all 256 positions, plus one fresh decode query at position 255."""
-    return build("tiny_fp32_1x256_d64", kv_dtype="f32", q_dtype="f32",
+    return build(NAMES[1], kv_dtype="f32", q_dtype="f32",
                  num_q_heads=1, num_kv_heads=1, head_dim=64, ctx_lens=[256],
                  calls=[Call("prefill", [0], [256]), Call("decode", [0], [1])],
                  seed=1001, scale=1.0 / 8.0)
@@ -174,7 +182,7 @@ def tiny_fp32() -> Workload:
 
 def batched_decode_bf16() -> Workload:
     """32 sequences, lengths U{128..2048}, 32 q heads / 8 KV heads, d=128."""
-    return build("decode_bf16_32seq_len128-2048_gqa4_d128", kv_dtype="bf16",
+    return build(NAMES[2], kv_dtype="bf16",
                  q_dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
                  ctx_len_range=(128, 2048), num_seqs=32,
                  calls=[Call("decode", list(range(32)), [1] * 32)], seed=1002)
@@ -182,14 +190,14 @@ def batched_decode_bf16() -> Workload:
 
 def causal_prefill_bf16() -> Workload:
     """4 sequences x 4096 tokens, causal prefill, 32 q heads / 8 KV heads, d=128."""
-    return build("prefill_bf16_4x4096_gqa4_d128", kv_dtype="bf16", q_dtype="bf16",
+    return build(NAMES[3], kv_dtype="bf16", q_dtype="bf16",
                  num_q_heads=32, num_kv_heads=8, head_dim=128, ctx_lens=[4096] * 4,
                  calls=[Call("prefill", [0, 1, 2, 3], [4096] * 4)], seed=1003)
 
 
 def long_decode_bf16() -> Workload:
     """8 sequences x 32768 tokens, 64 q heads / 8 KV heads, d=128, one query each."""
-    return build("decode_bf16_8x32768_gqa8_d128", kv_dtype="bf16", q_dtype="bf16",
+    return build(NAMES[4], kv_dtype="bf16", q_dtype="bf16",
                  num_q_heads=64, num_kv_heads=8, head_dim=128, ctx_lens=[32768] * 8,
                  calls=[Call("decode", list(range(8)), [1] * 8)], seed=1004)
 
@@ -198,7 +206,7 @@ def mixed_fp8() -> Workload:
     """16 sequences sharing a 1024-token prefix plus 512 own tokens each; fp8
     KV pool with one scale per page; sequences 0-7 run a 256-token chunked
     prefill (their last 256 positions), sequences 8-15 decode one token."""
-    return build("mixed_fp8kv_16x1536_prefix1024_gqa4_d128", kv_dtype="fp8",
+    return build(NAMES[5], kv_dtype="fp8",
                  q_dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
                  ctx_lens=[1536] * 16, shared_prefix=1024,
                  calls=[Call("prefill", list(range(8)), [256] * 8),
