@@ -170,6 +170,32 @@ def test_matches_torch_sdpa(chunk):
     np.testing.assert_allclose(O, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
 
 
+def test_sampled_rows_match_torch_sdpa():
+    """The row-sampling oracle (used at full sizes) against PyTorch's CPU SDPA in
+    float64 on a two-sequence chunked batch, rows drawn from both sequences and
+    from heads of different KV groups."""
+    wl = workloads.small("prefill", kv_dtype="bf16", num_q_heads=4, num_kv_heads=2,
+                         head_dim=32, ctx_lens=(45, 70), q_lens=(45, 19), seed=21)
+    call = wl.calls[0]
+    pool = _pool_for(wl)
+    rows = [(0, 0), (44, 3), (45, 1), (50, 2), (63, 3)]
+    O, L = oracle.paged_attention_rows(pool, call.q, call.cu_q_lens, call.ctx_lens,
+                                       call.block_table, wl.num_q_heads, wl.scale, rows)
+    cu = [0, 45, 64]
+    for n, (t, h) in enumerate(rows):
+        b = 0 if t < 45 else 1
+        k, v = _src_tokens(wl, b)
+        ctx, n_q = wl.ctx_lens[b], cu[b + 1] - cu[b]
+        pos = ctx - n_q + (t - cu[b])
+        q = call.q[t, h].to(torch.float64)[None, None]            # [1, 1, d]
+        kk, vv = k[:, h // 2][None], v[:, h // 2][None]           # [1, ctx, d]
+        mask = (torch.arange(ctx) <= pos)[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, attn_mask=mask, scale=wl.scale)
+        np.testing.assert_allclose(O[n], ref[0, 0].numpy(), rtol=0, atol=1e-12)
+        s = wl.scale * (k[: pos + 1, h // 2] @ call.q[t, h].to(torch.float64))
+        assert abs(L[n] - float(torch.logsumexp(s, 0))) < 1e-12
+
+
 # ---------------------------------------------------------------- P-g
 def test_zero_query_gives_mean_of_visible_v():
     rng = np.random.default_rng(1)
