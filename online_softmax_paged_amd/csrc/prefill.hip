@@ -427,60 +427,92 @@ struct DmaSmem {
 // callers wait with wait_vmcnt<>() before the data is used.  The instruction
 // writes no register, and s_nop covers the M0-write -> LDS-DMA hazard.
 __device__ __forceinline__ void dma16(const void* base, int32_t nbytes, uint32_t voffset,
-                                      const void* lds) {
+                                      uint32_t lds_addr) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))),
                     __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffff)),
                     __builtin_amdgcn_readfirstlane(nbytes), kRsrcWord3};
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)lds)));
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rs), "{m0}"(m0)
                : "memory");
 }
 
-// Instruction u (0 .. D/8 - 1) of a tile is issued by wave u % NW: the first
-// D/16 move K (1 KiB each), the rest move V^T.
+// The DMA instructions of one tile form four groups of D/32 (1 KiB each):
+// K page 0, K page 1, V^T page 0, V^T page 1.  Instruction u = i*NW + wave
+// is this wave's i-th.  Its lane offset inside the page chunk and its LDS
+// offset inside a stage are the same for every tile, so they are computed
+// once; per tile only the two page addresses and valid lengths change.
+template <int D, int NW>
+struct DmaPlan {
+  static constexpr int PER = D / 32;              // instructions per group
+  static constexpr int TOT = 4 * PER;             // instructions per tile
+  static constexpr int NI = (TOT + NW - 1) / NW;  // instructions per wave
+  uint32_t voff[NI];
+  int group[NI];
+  int lds[NI];
+  int count;
+
+  __device__ __forceinline__ DmaPlan(int wave, int lane) {
+    constexpr int CPR = D / 8;  // 16-byte chunks per K row
+    constexpr int PAGE_BYTES = kPage * D * 2;
+    count = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int u = i * NW + wave;
+      // with PER == NW the group of instruction i does not depend on the wave
+      const int grp = (PER == NW) ? i : u / PER;
+      const int sub = (PER == NW) ? wave : u % PER;
+      const int m = sub * 64 + lane;  // 16-byte slot inside the group's LDS region
+      uint32_t vo;
+      if (grp < 2) {
+        // K row rr of page grp, LDS position pos holds logical chunk pos ^ (row % CPR)
+        const int rr = m / CPR, pos = m % CPR;
+        vo = (rr * CPR + (pos ^ ((grp * kPage + rr) % CPR))) * 16;
+      } else {
+        // V^T row d of the page: slot e' holds keys 8e..8e+7, e = e' ^ ((d / 8) % 2)
+        const int d = m >> 1, e = (m & 1) ^ ((d >> 3) & 1);
+        vo = (d * 2 + e) * 16;
+      }
+      voff[i] = vo;
+      group[i] = grp;
+      lds[i] = grp * PAGE_BYTES + sub * 1024;
+      count += u < TOT ? 1 : 0;
+    }
+  }
+};
+
+// The LDS address (offset in the workgroup's LDS) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
 template <int D, int NW>
 __device__ __forceinline__ void dma_tile(const AttnArgs& a, int g, const TilePages& tp, int t,
-                                         int ctx, char* stage, int wave, int lane) {
-  constexpr int CPR = D / 8;            // 16-byte chunks per K row
-  constexpr int NK = D / 16;            // K instructions per tile (= V instructions)
+                                         int ctx, uint32_t stage, const DmaPlan<D, NW>& plan) {
   constexpr int PAGE_BYTES = kPage * D * 2;
+  int64_t off[2];
+  int knb[2], vnb[2];
 #pragma unroll
-  for (int u0 = 0; u0 < 2 * NK; u0 += NW) {
-    const int u = u0 + wave;
-    if (u >= 2 * NK) break;
-    if (u < NK) {
-      // --- K: LDS chunk m = u*64 + lane -> (row r, position p)
-      const int m = u * 64 + lane;
-      const int r = m / CPR, pos = m % CPR;
-      const int logical = pos ^ (r % CPR);
-      const bool pg = (u * 64 / CPR) / kPage;  // uniform per instruction
-      const int tok = r % kPage;
-      const int page_tok0 = t * kKeys + (pg ? kPage : 0);
-      const bool ok = pg ? tp.ok[1] : tp.ok[0];
-      const int n_valid = ok ? max(0, min(kPage, ctx - page_tok0)) : 0;
-      const int64_t chunk =
-          ok ? static_cast<int64_t>(pg ? tp.phys[1] : tp.phys[0]) * a.num_kv_heads + g : 0;
-      dma16(static_cast<const char*>(a.k) + chunk * PAGE_BYTES, n_valid * D * 2,
-            (tok * CPR + logical) * 16, stage + u * 1024);
-    } else {
-      // --- V^T: LDS chunk m = (u-NK)*64 + lane -> page, row d, position e'
-      const int uv = u - NK;
-      const int m = uv * 64 + lane;
-      const bool pg = (uv * 64) / (2 * D);     // uniform per instruction
-      const int mm = m % (2 * D);
-      const int d = mm >> 1, ep = mm & 1;
-      const int e = ep ^ ((d >> 3) & 1);
-      const int page_tok0 = t * kKeys + (pg ? kPage : 0);
-      const bool ok = (pg ? tp.ok[1] : tp.ok[0]) && page_tok0 < ctx;
-      const int64_t chunk =
-          ok ? static_cast<int64_t>(pg ? tp.phys[1] : tp.phys[0]) * a.num_kv_heads + g : 0;
-      dma16(static_cast<const char*>(a.v) + chunk * PAGE_BYTES, ok ? PAGE_BYTES : 0,
-            (d * 2 + e) * 16, stage + DmaSmem<D>::KB + uv * 1024);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const int tok0 = t * kKeys + j * kPage;
+    const bool ok = tp.ok[j];
+    const int n_valid = min(kPage, max(0, ctx - tok0));
+    off[j] = ok ? (static_cast<int64_t>(tp.phys[j]) * a.num_kv_heads + g) * PAGE_BYTES : 0;
+    knb[j] = ok ? n_valid * D * 2 : 0;
+    vnb[j] = ok && n_valid > 0 ? PAGE_BYTES : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < DmaPlan<D, NW>::NI; ++i) {
+    if (DmaPlan<D, NW>::NI * NW != DmaPlan<D, NW>::TOT && i >= plan.count) break;
+    const int grp = plan.group[i];
+    const bool is_v = grp >= 2, hi = grp & 1;
+    const char* base = (is_v ? static_cast<const char*>(a.v) : static_cast<const char*>(a.k)) +
+                       (hi ? off[1] : off[0]);
+    const int nb = is_v ? (hi ? vnb[1] : vnb[0]) : (hi ? knb[1] : knb[0]);
+    dma16(base, nb, plan.voff[i], stage + plan.lds[i]);
   }
 }
 
@@ -525,8 +557,14 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   const int TQ = ROWS / G;
   constexpr int STAGE = DmaSmem<D>::STAGE;
   constexpr int CPR = D / 8;
-  // DMA instructions this wave issues per tile
-  const int my_dma = (D / 8 - wave + NW - 1) / NW;
+  const DmaPlan<D, NW> plan(wave, lane);
+  // wait until at most one tile's DMA of this wave is still in flight
+  auto wait_own_dma = [&]() {
+    if constexpr (DmaPlan<D, NW>::NI * NW == DmaPlan<D, NW>::TOT)
+      wait_vmcnt<DmaPlan<D, NW>::NI>();
+    else
+      wait_vmcnt_upto4(plan.count);
+  };
 
   const int q0 = a.cu_q_lens[b];
   const int qlen = a.cu_q_lens[b + 1] - q0;
@@ -571,8 +609,9 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     r.id[1] = __builtin_amdgcn_readlane(idv, (2 * t + 1) & 63);
     return check_pages(a, r, t, n_pages);
   };
-  dma_tile<D, NW>(a, g, tile_pages(0), 0, ctx, sm.buf, wave, lane);
-  dma_tile<D, NW>(a, g, tile_pages(1), 1, ctx, sm.buf + STAGE, wave, lane);
+  const uint32_t lds0 = lds_address(sm.buf);
+  dma_tile<D, NW>(a, g, tile_pages(0), 0, ctx, lds0, plan);
+  dma_tile<D, NW>(a, g, tile_pages(1), 1, ctx, lds0 + STAGE, plan);
 
   bf16x8 qf[D / 16];
   {
@@ -591,11 +630,13 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  wait_vmcnt_upto4(my_dma);  // tile 0 landed (tile 1 may still be in flight)
+  wait_own_dma();  // tile 0 landed (tile 1 may still be in flight)
   __syncthreads();
 
+  // stage of tile kt and of tile kt + 2 (three stages in rotation)
+  int st_cur = 0, st_pre = 2;
   for (int kt = 0; kt < n_kt; ++kt) {
-    char* stg = sm.buf + (kt % 3) * STAGE;
+    char* stg = sm.buf + st_cur * STAGE;
     if (kt == tail_tile) {
       // zero V^T slots of tokens at or past the context end in this stage
       uint16_t* vt = reinterpret_cast<uint16_t*>(stg + DmaSmem<D>::KB);
@@ -611,8 +652,9 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     }
     // DMA tile kt+2 into the stage tile kt-1 used (all waves are past it)
     if (kt + 2 < n_kt)
-      dma_tile<D, NW>(a, g, tile_pages(kt + 2), kt + 2, ctx, sm.buf + ((kt + 2) % 3) * STAGE,
-                      wave, lane);
+      dma_tile<D, NW>(a, g, tile_pages(kt + 2), kt + 2, ctx, lds0 + st_pre * STAGE, plan);
+    st_cur = st_cur == 2 ? 0 : st_cur + 1;
+    st_pre = st_pre == 2 ? 0 : st_pre + 1;
 
     // S^T = K . Q^T
     const char* kbase = stg + col * (D * 2);
@@ -650,13 +692,13 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
       m = m_new;
       mu = m == -INFINITY ? 0.f : m;
     }
-    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sv[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -mu));
-      psum += sv[i];
-    }
-    l += psum;
+    for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -mu));
+    // row sum in four independent chains
+    float ps[4] = {sv[0], sv[1], sv[2], sv[3]};
+#pragma unroll
+    for (int i = 4; i < 16; ++i) ps[i & 3] += sv[i];
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // O^T += V^T . P^T, page c = keys 16c..16c+15 of the tile
     const char* vbase = stg + DmaSmem<D>::KB;
@@ -680,7 +722,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
       }
     }
     // tile kt+1 must have landed before the barrier; tile kt+2 may still fly
-    if (kt + 2 < n_kt) wait_vmcnt_upto4(my_dma); else wait_vmcnt<0>();
+    if (kt + 2 < n_kt) wait_own_dma(); else wait_vmcnt<0>();
     __syncthreads();
   }
 
