@@ -425,7 +425,10 @@ struct DmaSmem {
 // asm so the compiler's wait-count pass does not drain all outstanding loads
 // before each write of M0 (the hardware latches M0 when the load issues);
 // callers wait with wait_vmcnt<>() before the data is used.  The instruction
-// writes no register, and s_nop covers the M0-write -> LDS-DMA hazard.
+// writes no register.  The compiler's hazard pass does not look inside inline
+// asm, so the asm carries its own wait states: s_nop 4 (five) covers both a
+// VALU write of a descriptor SGPR (v_readfirstlane) before a vector-memory
+// read of it (five wait states) and an M0 write before an LDS DMA (one).
 __device__ __forceinline__ void dma16(const void* base, int32_t nbytes, uint32_t voffset,
                                       uint32_t lds_addr) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
@@ -433,7 +436,7 @@ __device__ __forceinline__ void dma16(const void* base, int32_t nbytes, uint32_t
                     __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffff)),
                     __builtin_amdgcn_readfirstlane(nbytes), kRsrcWord3};
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rs), "{m0}"(m0)
                : "memory");
@@ -524,7 +527,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Same, for a wave-uniform count known only at run time (0..4).
-__device__ __forceinline__ void wait_vmcnt_upto4(int n) {
+[[maybe_unused]] __device__ __forceinline__ void wait_vmcnt_upto4(int n) {
   switch (n) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<1>(); break;
@@ -542,17 +545,23 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-  // Workgroups are dealt to the 8 dies (XCDs, each with its own L2) round
-  // robin by linear id.  Remap so die k runs a contiguous range of tasks
-  // ordered (sequence x KV head)-major, query tiles longest first: a die then
-  // streams about one (sequence, KV head)'s K/V at a time, which fits its L2.
+  // Workgroups are dealt to the 8 dies (XCDs, each with its own 4 MB L2)
+  // round robin by linear id.  When the (sequence, KV head) pairs split evenly
+  // over the dies, die k takes pairs k*P .. k*P+P-1 and runs them two at a
+  // time (about 4 MiB of K/V in flight, the size of its L2), longest query
+  // tiles first across both pairs, so every die ends on short tiles.
   const int n_bg = gridDim.x;
-  const int n_tasks = n_bg * n_tiles;
   const int lin = blockIdx.y * n_bg + blockIdx.x;
-  const int task = (n_tasks % 8 == 0) ? (lin % 8) * (n_tasks / 8) + lin / 8 : lin;
-  const int bg = (n_tasks % 8 == 0) ? task / n_tiles : blockIdx.x;
+  int bg = blockIdx.x, tile_from_end = blockIdx.y;
+  if (n_bg % 8 == 0) {
+    const int P = n_bg / 8, GP = (P % 2 == 0) ? 2 : 1;
+    const int j = lin / 8, per_group = GP * n_tiles;
+    const int grp = j / per_group, i = j % per_group;
+    bg = (lin % 8) * P + grp * GP + i % GP;
+    tile_from_end = i / GP;
+  }
   const int b = bg / Hkv, g = bg % Hkv;
-  const int tile = n_tiles - 1 - ((n_tasks % 8 == 0) ? task % n_tiles : static_cast<int>(blockIdx.y));
+  const int tile = n_tiles - 1 - tile_from_end;
   constexpr int ROWS = 32 * NW;   // query rows per workgroup
   const int TQ = ROWS / G;
   constexpr int STAGE = DmaSmem<D>::STAGE;
