@@ -265,10 +265,11 @@ void decode_split_kernel(AttnArgs a) {
   }
 }
 
-// fp32 pools: one wave per (query head, sequence, page range); lane owns
-// features lane and lane + 64.  Plain FMA arithmetic with wave reductions.
+// fp32 pools: one wave per (query head, sequence, page range), 64 keys per
+// step (see f32_attend).
 template <int D>
 __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
+  __shared__ float qs[kWaves][D];
   const int split = blockIdx.x, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * kWaves + wave;
@@ -282,39 +283,20 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
   const int t_begin = split * pps * kPage;
   const int t_end = min(t_begin + pps * kPage, ctx);
   constexpr int NPL = D / 64;  // features per lane
-  const float* qp = static_cast<const float*>(a.q) + (static_cast<int64_t>(b) * Hq + h) * D;
-  float q[NPL], o[NPL];
+  const int64_t row = static_cast<int64_t>(b) * Hq + h;
+  const float* qp = static_cast<const float*>(a.q) + row * D;
+  float o[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    q[j] = qp[lane + 64 * j];
+    qs[wave][lane + 64 * j] = qp[lane + 64 * j];
     o[j] = 0.f;
   }
-  const float* kb = static_cast<const float*>(a.k);
-  const float* vb = static_cast<const float*>(a.v);
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const float sc = a.scale * kLog2e;
+  __builtin_amdgcn_wave_barrier();
   float m = -INFINITY, l = 0.f;
-  for (int t = t_begin; t < t_end; ++t) {
-    const int32_t phys = bt[t / kPage];
-    if (!valid_block(phys, a.num_blocks)) continue;
-    const int64_t chunk = (static_cast<int64_t>(phys) * Hkv + g) * kPage * D;
-    float dot = 0.f;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) dot += q[j] * kb[chunk + (t % kPage) * D + lane + 64 * j];
-    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s);
-    const float s2 = dot * sc;
-    const float m_new = fmaxf(m, s2);
-    const float alpha = fast_exp2(m - m_new);
-    const float pr = fast_exp2(s2 - m_new);
-    l = l * alpha + pr;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      o[j] = o[j] * alpha + pr * vb[chunk + (lane + 64 * j) * kPage + t % kPage];
-    m = m_new;
-  }
+  f32_attend<D>(a, a.block_table + static_cast<int64_t>(b) * a.bt_stride, g, qs[wave], t_begin,
+                t_end, lane, o, m, l);
   const bool empty = !(l > 0.f);
   const float lse = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
-  const int64_t row = static_cast<int64_t>(b) * Hq + h;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const float out = empty ? 0.f : o[j] / l;

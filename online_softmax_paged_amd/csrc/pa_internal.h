@@ -123,6 +123,89 @@ struct AttnArgs {
   float* ws_lse;               // decode: [B, Hq, S] partial logsumexp
 };
 
+// Full-wave max and sum (64 lanes).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s);
+  return x;
+}
+
+// fp32 pools: one wave folds keys [t0, t1) of one sequence (t0 a multiple of
+// 16, so 64 keys are four whole pages) into the online-softmax state of one
+// query row q (d floats in LDS, read by every lane).  Scores take one key per
+// lane; P.V takes one feature per lane (two for d = 128), the key weights
+// broadcast from their lanes.  o is unnormalised, m is in log2 units of the
+// scaled scores.  Keys on invalid pages or at or past t1 get weight 0 and
+// their V values are replaced by 0 before use (the pool may hold NaN there).
+template <int D>
+__device__ __forceinline__ void f32_attend(const AttnArgs& a, const int32_t* bt, int g,
+                                           const float* q, int t0, int t1, int lane,
+                                           float (&o)[D / 64], float& m, float& l) {
+  const float* kb = static_cast<const float*>(a.k);
+  const float* vb = static_cast<const float*>(a.v);
+  const int Hkv = a.num_kv_heads;
+  const float sc = a.scale * kLog2e;
+  for (int base = t0; base < t1; base += 64) {
+    const int t = base + lane;
+    const int32_t phys = t < t1 ? bt[t / kPage] : -1;
+    const bool ok = t < t1 && phys >= 0 && phys < a.num_blocks;
+    float s = -INFINITY;
+    if (ok) {
+      const float* kr = kb + ((static_cast<int64_t>(phys) * Hkv + g) * kPage + t % kPage) * D;
+      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < D; i += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(kr + i);
+        const float4 qv = *reinterpret_cast<const float4*>(q + i);
+        d0 = __builtin_fmaf(kv.x, qv.x, d0);
+        d1 = __builtin_fmaf(kv.y, qv.y, d1);
+        d2 = __builtin_fmaf(kv.z, qv.z, d2);
+        d3 = __builtin_fmaf(kv.w, qv.w, d3);
+      }
+      s = ((d0 + d1) + (d2 + d3)) * sc;
+    }
+    const float m_new = fmaxf(m, wave_max(s));
+    if (m_new == -INFINITY) continue;  // nothing visible yet (uniform)
+    const float alpha = fast_exp2(m - m_new);
+    const float p = fast_exp2(s - m_new);
+    l = l * alpha + wave_sum(p);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) o[j] *= alpha;
+    m = m_new;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int start = base + pp * kPage;
+      if (start >= t1) break;
+      const int nv = min(kPage, t1 - start);
+      const int32_t pid = __builtin_amdgcn_readlane(phys, pp * kPage);
+      if (pid < 0 || pid >= a.num_blocks) continue;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        const float* vr = vb + ((static_cast<int64_t>(pid) * Hkv + g) * D + lane + 64 * j) * kPage;
+        float v[kPage];
+#pragma unroll
+        for (int c = 0; c < kPage; c += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(vr + c);
+          v[c] = x.x; v[c + 1] = x.y; v[c + 2] = x.z; v[c + 3] = x.w;
+        }
+        float acc = o[j];
+#pragma unroll
+        for (int k = 0; k < kPage; ++k) {
+          const float pk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), pp * kPage + k));
+          acc = __builtin_fmaf(pk, k < nv ? v[k] : 0.f, acc);
+        }
+        o[j] = acc;
+      }
+    }
+  }
+}
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t st);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t st);
 

@@ -752,10 +752,11 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   if (half == 0 && a.lse) a.lse[qrow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
 }
 
-// fp32 pools: one wave per (query row, query head); lane owns features lane
-// and lane + 64; plain FMA arithmetic, online softmax one key at a time.
+// fp32 pools: one wave per (query row, query head), 64 keys per step (see
+// f32_attend).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
+  __shared__ float qs[4][D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave, h = blockIdx.y, b = blockIdx.z;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, g = h / G;
@@ -769,35 +770,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
   constexpr int NPL = D / 64;
   const int64_t row = static_cast<int64_t>(q0 + i) * Hq + h;
   const float* qp = static_cast<const float*>(a.q) + row * D;
-  float q[NPL], o[NPL];
+  float o[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    q[j] = qp[lane + 64 * j];
+    qs[wave][lane + 64 * j] = qp[lane + 64 * j];
     o[j] = 0.f;
   }
-  const float* kb = static_cast<const float*>(a.k);
-  const float* vb = static_cast<const float*>(a.v);
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const float sc = a.scale * kLog2e;
+  // the row is written and read by this wave only (LDS operations of a wave
+  // complete in order)
+  __builtin_amdgcn_wave_barrier();
   float m = -INFINITY, l = 0.f;
-  for (int t = 0; t < t_end; ++t) {
-    const int32_t phys = bt[t / kPage];
-    if (phys < 0 || phys >= a.num_blocks) continue;
-    const int64_t chunk = (static_cast<int64_t>(phys) * Hkv + g) * kPage * D;
-    float dot = 0.f;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) dot += q[j] * kb[chunk + (t % kPage) * D + lane + 64 * j];
-    for (int s = 32; s >= 1; s >>= 1) dot += __shfl_xor(dot, s);
-    const float s2 = dot * sc;
-    const float m_new = fmaxf(m, s2);
-    const float alpha = fast_exp2(m - m_new);
-    const float pr = fast_exp2(s2 - m_new);
-    l = l * alpha + pr;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      o[j] = o[j] * alpha + pr * vb[chunk + (lane + 64 * j) * kPage + t % kPage];
-    m = m_new;
-  }
+  f32_attend<D>(a, a.block_table + static_cast<int64_t>(b) * a.bt_stride, g, qs[wave], 0,
+                max(t_end, 0), lane, o, m, l);
   const bool empty = !(l > 0.f);
   float* op = static_cast<float*>(a.o) + row * D;
 #pragma unroll
