@@ -101,7 +101,7 @@ template <int D, bool FP8, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
 void decode_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, grp = lane >> 4;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
   const int S = a.num_splits;
@@ -192,21 +192,36 @@ void decode_split_kernel(AttnArgs a) {
   // length (entries past the sequence's last page are read, never used), and
   // ring slots past the last page load from an empty buffer (no traffic), so
   // every load is unconditional and the compiler can count those in flight.
+  // The ids of the first 64 pages and the first three pages are requested
+  // before the context length arrives, so the first data waits for two
+  // dependent reads (table, page) rather than three.
   const int first = p_begin + wave;
   const int range_end = min(p_begin + pps, max_pages);
   const int n_spec = first < range_end ? (range_end - first + kWaves - 1) / kWaves : 0;
+  const int32_t id0 = lane < min(64, n_spec) ? bt[first + kWaves * lane] : -1;
+  KVFrag<D> fa, fb, fc;
+  {
+    auto spec_at = [&](int i) -> int32_t {
+      return i < n_spec ? __builtin_amdgcn_readlane(id0, i) : -1;
+    };
+    load_page<D, FP8, NT>(fa, a, spec_at(0), g, lane);
+    load_page<D, FP8, NT>(fb, a, spec_at(1), g, lane);
+    load_page<D, FP8, NT>(fc, a, spec_at(2), g, lane);
+  }
   const int n_mine = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
   for (int i0 = 0; i0 < n_mine; i0 += 64) {
     const int n = min(64, n_mine - i0);
-    int32_t my_id = lane < min(64, n_spec - i0) ? bt[first + kWaves * (i0 + lane)] : -1;
+    int32_t my_id = i0 == 0 ? id0
+                            : (lane < min(64, n_spec - i0) ? bt[first + kWaves * (i0 + lane)] : -1);
     my_id = lane < n ? my_id : -1;
     auto id_at = [&](int i) -> int32_t {
       return i < n ? __builtin_amdgcn_readlane(my_id, min(i, 63)) : -1;
     };
-    KVFrag<D> fa, fb, fc;
-    load_page<D, FP8, NT>(fa, a, id_at(0), g, lane);
-    load_page<D, FP8, NT>(fb, a, id_at(1), g, lane);
-    load_page<D, FP8, NT>(fc, a, id_at(2), g, lane);
+    if (i0 > 0) {
+      load_page<D, FP8, NT>(fa, a, id_at(0), g, lane);
+      load_page<D, FP8, NT>(fb, a, id_at(1), g, lane);
+      load_page<D, FP8, NT>(fc, a, id_at(2), g, lane);
+    }
     for (int i = 0; i < n; i += 3) {
       const int pa_ = first + kWaves * (i0 + i);
       process(fa, pa_, valid_block(id_at(i), a.num_blocks));
