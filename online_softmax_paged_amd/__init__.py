@@ -25,7 +25,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 BLOCK_SIZE = 16
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m online_softmax_paged_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built: run `python online_softmax_paged_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 

@@ -1,6 +1,6 @@
 """Build libpa.so in-tree with hipcc for gfx950.
 
-    python -m online_softmax_paged_amd.build
+    python online_softmax_paged_amd/build.py
 
 Every call recompiles all sources (objects go to _build/, ignored by git).
 """

@@ -231,7 +231,7 @@ def test_repeat_runs_are_bitwise_equal_and_splits_agree():
         b = dc.run(pool, num_splits=s)
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     ro, rl = H.oracle_call(H.oracle_pool(wl), wl, wl.calls[0])
-    for s in (1, 2, 3, 7, 16, 125):
+    for s in (1, 2, 3, 7, 16, 64):
         eo, el = H.max_err(*dc.run(pool, num_splits=s), ro, rl)
         assert eo <= 2e-2 and el <= 1e-4, (s, eo, el)
     wl2 = workloads.small("prefill", num_q_heads=8, num_kv_heads=2, ctx_lens=(500, 70), seed=63)
@@ -239,6 +239,26 @@ def test_repeat_runs_are_bitwise_equal_and_splits_agree():
     dc2 = H.DeviceCall(wl2, wl2.calls[0])
     a, b = dc2.run(pool2), dc2.run(pool2)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_reused_workspace_gives_the_same_results():
+    """One workspace serves consecutive calls of different batches (and
+    dtypes), bit-identical to a fresh workspace each time."""
+    _log("decode workspace reuse")
+    cases = [workloads.small("decode", num_q_heads=16, num_kv_heads=2, ctx_lens=(2000, 900, 31), seed=64),
+             workloads.small("decode", num_q_heads=8, num_kv_heads=2, ctx_lens=(300, 45), seed=65),
+             workloads.small("decode", kv_dtype="fp8", num_q_heads=8, num_kv_heads=2,
+                             ctx_lens=(1000, 17, 400), seed=66)]
+    S = 6
+    need = max(pa.decode_workspace_bytes(len(wl.ctx_lens), wl.num_q_heads, wl.head_dim, S) for wl in cases)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")   # arbitrary contents
+    for rep in range(2):
+        for wl in cases:
+            pool = H.device_pool(wl)
+            dc = H.DeviceCall(wl, wl.calls[0])
+            fresh = dc.run(pool, num_splits=S)
+            reused = dc.run(pool, num_splits=S, workspace=ws)
+            assert torch.equal(fresh[0], reused[0]) and torch.equal(fresh[1], reused[1]), (rep, wl.name)
 
 
 def test_table_entries_past_the_end_are_never_read():
