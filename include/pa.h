@@ -107,7 +107,8 @@ int32_t pa_abi_version(void);
  *   0) where amax is the largest |value| this call writes into that block (all
  *   heads, dims, tokens), and each value becomes the nearest-even E4M3 code of
  *   clamp(x / s, -448, 448).  So a block must be written whole by one call;
- *   earlier codes of a block touched again are not re-quantised.
+ *   earlier codes of a block touched again are not re-quantised (use
+ *   pa_append_kv for that).
  * workspace: device memory of pa_write_kv_workspace_bytes(pool) bytes
  *   (0 for non-fp8 pools; may then be NULL).  Slots must be distinct.
  */
@@ -115,6 +116,37 @@ size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool);
 pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
                       pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ append
+ * Like pa_write_kv, for tokens appended to sequences whose last page may be
+ * partly filled (one new token per sequence per decode step, as the survey
+ * page's section 3 describes: new tokens go to the sequence's current block,
+ * and a new block is taken when it is full).  In every page this call writes,
+ * the offsets below the lowest offset it writes are the page's existing
+ * tokens and are kept; the call must write a page's new tokens as a run of
+ * offsets from that lowest one.
+ * Pool f32 / bf16: identical to pa_write_kv.
+ * Pool fp8: each touched page gets a new K and V scale s' = amax' / 448 (1 when
+ *   amax' is 0), where amax' is the largest |value| among the page's existing
+ *   tokens as stored (code * old scale, float32) and the new tokens (all
+ *   heads); the existing codes are re-encoded as the nearest-even E4M3 code of
+ *   clamp(code * old scale / s'), then the new tokens are encoded with s'.
+ * Same arguments, workspace and errors as pa_write_kv.
+ */
+pa_status pa_append_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                       pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ copy
+ * Copy whole physical blocks: block dst_blocks[i] becomes a bit-exact copy of
+ * block src_blocks[i] (K and V of every KV head, and the fp8 scales).  The
+ * copy a sequence needs before writing into a block it shares with others
+ * (copy on write; see pa_plan_append).  src_blocks, dst_blocks: int32
+ * [num_pairs] (device).  Destinations must be distinct and must not be
+ * sources of the same call.  Ids outside [0, num_blocks) are skipped.
+ */
+pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t num_pairs, void* stream);
 
 /* ------------------------------------------------------------------ gather
  * Copy each sequence's logical tokens out of the pool, through its block
@@ -203,6 +235,27 @@ pa_status pa_block_incref(pa_allocator* a, int32_t block);
 pa_status pa_block_decref(pa_allocator* a, int32_t block);
 int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
 int32_t pa_num_free_blocks(const pa_allocator* a);
+
+/*
+ * Plan appending num_new[b] tokens to each sequence b (host memory throughout;
+ * survey page section 3: blocks on demand, copy of a shared block before a
+ * sequence writes into it).  Position p = ctx_lens[b] + i of sequence b goes to
+ * page p / 16, offset p % 16.  A position that starts a page takes a fresh
+ * block (lowest free id).  When the partly filled last page of a sequence is
+ * shared (refcount > 1), the sequence first gets a fresh block: the pair
+ * (shared, fresh) is written to copy_src / copy_dst (copy it with
+ * pa_copy_blocks before appending) and the shared block loses one reference.
+ * On success block_table rows and ctx_lens are updated in place,
+ * slot_mapping[sum of num_new] holds the slots in sequence order (the order of
+ * the rows of k_new / v_new for pa_append_kv), and *num_copies the pairs
+ * written.  Checks come first: PA_ERR_INVALID_ARG (bad length, table too
+ * narrow, last page not allocated, more copies than max_copies),
+ * PA_ERR_OOM (not enough free blocks); on any error nothing is changed.
+ */
+pa_status pa_plan_append(pa_allocator* a, int32_t* block_table, int32_t bt_stride,
+                         int32_t* ctx_lens, const int32_t* num_new, int32_t num_seqs,
+                         int32_t* slot_mapping, int32_t* copy_src, int32_t* copy_dst,
+                         int32_t max_copies, int32_t* num_copies);
 
 #ifdef __cplusplus
 }

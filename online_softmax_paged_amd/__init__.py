@@ -66,11 +66,16 @@ _incref = _sig("pa_block_incref", ctypes.c_int, [_VP, _I32])
 _decref = _sig("pa_block_decref", ctypes.c_int, [_VP, _I32])
 _refcount = _sig("pa_block_refcount", _I32, [_VP, _I32])
 _num_free = _sig("pa_num_free_blocks", _I32, [_VP])
+_append = _sig("pa_append_kv", ctypes.c_int, [_P, _VP, _VP, ctypes.c_int, _VP, _I32, _VP, _SZ, _VP])
+_copy_blocks = _sig("pa_copy_blocks", ctypes.c_int, [_P, _VP, _VP, _I32, _VP])
+_plan_append = _sig("pa_plan_append", ctypes.c_int,
+                    [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP])
 
 EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes", "pa_write_kv",
             "pa_gather_kv", "pa_prefill", "pa_decode_num_splits", "pa_decode_workspace_bytes",
             "pa_decode", "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_block",
-            "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks"]
+            "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks",
+            "pa_append_kv", "pa_copy_blocks", "pa_plan_append"]
 
 
 class PAError(RuntimeError):
@@ -160,6 +165,26 @@ def write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mappin
     _check(_write(pool.c, _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], _ptr(slot_mapping), n,
                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
                   _stream(stream)), "pa_write_kv")
+
+
+def append_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+              workspace: torch.Tensor | None = None, stream=None):
+    """Append tokens to partly filled pages (fp8 pools re-quantise each touched page)."""
+    n = int(slot_mapping.numel())
+    need = write_kv_workspace_bytes(pool)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_new.device)
+    _check(_append(pool.c, _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], _ptr(slot_mapping), n,
+                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                   _stream(stream)), "pa_append_kv")
+
+
+def copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Device copy of whole blocks: dst[i] <- src[i] (int32 device tensors)."""
+    n = int(src.numel())
+    if n != int(dst.numel()):
+        raise ValueError("src and dst differ in length")
+    _check(_copy_blocks(pool.c, _ptr(src), _ptr(dst), n, _stream(stream)), "pa_copy_blocks")
 
 
 def gather_kv(pool: KVPool, block_table, ctx_lens, max_ctx_len: int, stream=None):
@@ -279,3 +304,23 @@ class BlockAllocator:
 
     def num_free(self) -> int:
         return int(_num_free(self._h))
+
+    def plan_append(self, block_table: torch.Tensor, ctx_lens: torch.Tensor, num_new):
+        """Host planning of an append (pa_plan_append).  block_table [B, W] and
+        ctx_lens [B] are contiguous int32 CPU tensors, updated in place.
+        Returns (slot_mapping int32 CPU tensor, copy_src, copy_dst int32 CPU
+        tensors of the blocks to copy before appending)."""
+        for t in (block_table, ctx_lens):
+            if t.device.type != "cpu" or t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("block_table and ctx_lens must be contiguous int32 CPU tensors")
+        B = int(ctx_lens.numel())
+        nn = torch.as_tensor(num_new, dtype=torch.int32).contiguous()
+        slots = torch.empty(max(1, int(nn.sum())), dtype=torch.int32)
+        csrc = torch.empty(max(1, B), dtype=torch.int32)
+        cdst = torch.empty(max(1, B), dtype=torch.int32)
+        nc = ctypes.c_int32(0)
+        _check(_plan_append(self._h, _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
+                            _ptr(nn), B, _ptr(slots), _ptr(csrc), _ptr(cdst), B,
+                            ctypes.byref(nc)), "pa_plan_append")
+        k = int(nn.sum())
+        return slots[:k], csrc[:nc.value], cdst[:nc.value]

@@ -95,12 +95,16 @@ int32_t pa_abi_version(void) { return 1; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
-  return 2 * sizeof(uint32_t) * static_cast<size_t>(pool->num_blocks);
+  return 3 * sizeof(uint32_t) * static_cast<size_t>(pool->num_blocks);
 }
 
-pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
-                      pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status write_or_append(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                          pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                          void* workspace, size_t workspace_bytes, bool append, void* stream) {
   pa_status s = check_pool(pool);
   if (s != PA_OK) return s;
   if (num_tokens < 0) return PA_ERR_INVALID_ARG;
@@ -115,8 +119,37 @@ pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_n
     return PA_ERR_UNSUPPORTED;
   }
   return launched(launch_write_kv(*pool, k_new, v_new, src_dtype, slot_mapping, num_tokens,
-                                  static_cast<uint32_t*>(workspace),
+                                  static_cast<uint32_t*>(workspace), append,
                                   static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return write_or_append(pool, k_new, v_new, src_dtype, slot_mapping, num_tokens, workspace,
+                         workspace_bytes, false, stream);
+}
+
+pa_status pa_append_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                       pa_dtype src_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return write_or_append(pool, k_new, v_new, src_dtype, slot_mapping, num_tokens, workspace,
+                         workspace_bytes, true, stream);
+}
+
+pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t num_pairs, void* stream) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_blocks || !dst_blocks) return PA_ERR_INVALID_ARG;
+  return launched(launch_copy_blocks(*pool, src_blocks, dst_blocks, num_pairs,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32_t bt_stride,

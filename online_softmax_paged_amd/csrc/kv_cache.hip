@@ -12,6 +12,11 @@
 // Quantising takes three passes: clear the per-block amax words, take the amax
 // of every written token into its block's word (atomic max on the float bits,
 // which order like the values for non-negative floats), then encode.
+//
+// Appending to a partly filled fp8 page changes its scale: the page's tokens
+// below the lowest offset the call writes are its existing tokens; their
+// stored values (code * old scale) join the amax, and they are re-encoded
+// with the new scale before the new tokens are encoded.
 #include "pa_internal.h"
 
 namespace pa {
@@ -58,15 +63,18 @@ __device__ __forceinline__ float load_src<uint16_t>(const uint16_t* p, int64_t i
   return bf16_bits_to_f32(p[i]);
 }
 
-// One workgroup per token: amax of its K values and of its V values.
+// One workgroup per token: amax of its K values and of its V values (and,
+// when appending, the lowest offset written to its page).
 template <typename S>
 __global__ void fp8_amax_kernel(const S* __restrict__ kn, const S* __restrict__ vn,
                                 const int32_t* __restrict__ slots, int32_t Hkv, int32_t D,
-                                int32_t num_blocks, uint32_t* __restrict__ amax_ws) {
+                                int32_t num_blocks, uint32_t* __restrict__ amax_ws,
+                                uint32_t* __restrict__ min_off) {
   const int64_t t = blockIdx.x;
   const int32_t slot = slots[t];
   const int32_t phys = slot >> 4;
   if (slot < 0 || phys >= num_blocks) return;
+  if (min_off && threadIdx.x == 0) atomicMin(&min_off[phys], static_cast<uint32_t>(slot & 15));
   const int64_t row = Hkv * D;
   float mk = 0.f, mv = 0.f;
   for (int64_t i = threadIdx.x; i < row; i += blockDim.x) {
@@ -154,6 +162,91 @@ __global__ void fp8_encode_kernel(uint8_t* __restrict__ kp, uint8_t* __restrict_
   }
 }
 
+// Appending, pass 3: the token at the lowest offset written to its page leads
+// the page: it folds the page's existing values (offsets below it, all heads,
+// as stored: code * old scale) into the page's amax words.
+__global__ void fp8_existing_amax_kernel(const uint8_t* __restrict__ kp,
+                                         const uint8_t* __restrict__ vp,
+                                         const float* __restrict__ k_scale,
+                                         const float* __restrict__ v_scale,
+                                         const int32_t* __restrict__ slots, int32_t Hkv,
+                                         int32_t D, int32_t num_blocks,
+                                         const uint32_t* __restrict__ min_off,
+                                         uint32_t* __restrict__ amax_ws) {
+  const int32_t slot = slots[blockIdx.x];
+  const int32_t phys = slot >> 4, off = slot & 15;
+  if (slot < 0 || phys >= num_blocks || static_cast<uint32_t>(off) != min_off[phys] || off == 0)
+    return;
+  const float sk = k_scale[phys], sv = v_scale[phys];
+  const int64_t base = static_cast<int64_t>(phys) * Hkv * kPage * D;
+  const int n = Hkv * off * D;  // existing values per pool
+  float mk = 0.f, mv = 0.f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int d = i % D, t = (i / D) % off, h = i / (D * off);
+    const int64_t chunk = base + static_cast<int64_t>(h) * kPage * D;
+    mk = fmaxf(mk, fabsf(__builtin_amdgcn_cvt_f32_fp8(kp[chunk + t * D + d], 0) * sk));
+    mv = fmaxf(mv, fabsf(__builtin_amdgcn_cvt_f32_fp8(vp[chunk + d * kPage + t], 0) * sv));
+  }
+  for (int s = 32; s >= 1; s >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, s));
+    mv = fmaxf(mv, __shfl_xor(mv, s));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&amax_ws[phys], __float_as_uint(mk));
+    atomicMax(&amax_ws[num_blocks + phys], __float_as_uint(mv));
+  }
+}
+
+// Appending, pass 4: the page leader re-encodes the page's existing codes with
+// the new scale (the old one is still in the scale arrays; the new tokens'
+// pass, which stores the new scale, runs after this one).
+__global__ void fp8_requant_kernel(uint8_t* __restrict__ kp, uint8_t* __restrict__ vp,
+                                   const float* __restrict__ k_scale,
+                                   const float* __restrict__ v_scale,
+                                   const int32_t* __restrict__ slots, int32_t Hkv, int32_t D,
+                                   int32_t num_blocks, const uint32_t* __restrict__ min_off,
+                                   const uint32_t* __restrict__ amax_ws) {
+  const int32_t slot = slots[blockIdx.x];
+  const int32_t phys = slot >> 4, off = slot & 15;
+  if (slot < 0 || phys >= num_blocks || static_cast<uint32_t>(off) != min_off[phys] || off == 0)
+    return;
+  const float sk_old = k_scale[phys], sv_old = v_scale[phys];
+  const float sk = fp8_scale_of(amax_ws[phys]), sv = fp8_scale_of(amax_ws[num_blocks + phys]);
+  const int64_t base = static_cast<int64_t>(phys) * Hkv * kPage * D;
+  const int n = Hkv * off * D;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int d = i % D, t = (i / D) % off, h = i / (D * off);
+    const int64_t chunk = base + static_cast<int64_t>(h) * kPage * D;
+    uint8_t* kq = kp + chunk + t * D + d;
+    uint8_t* vq = vp + chunk + d * kPage + t;
+    const float xk = __builtin_amdgcn_cvt_f32_fp8(*kq, 0) * sk_old;
+    const float xv = __builtin_amdgcn_cvt_f32_fp8(*vq, 0) * sv_old;
+    *kq = static_cast<uint8_t>(encode_fp8x4(to_code_domain(xk, sk), 0.f, 0.f, 0.f) & 0xff);
+    *vq = static_cast<uint8_t>(encode_fp8x4(to_code_domain(xv, sv), 0.f, 0.f, 0.f) & 0xff);
+  }
+}
+
+// Copy whole physical blocks (all heads, K and V, and the fp8 scales): one
+// thread per 16 bytes of a block's K (and the same 16 bytes of its V).
+__global__ void copy_blocks_kernel(char* __restrict__ kp, char* __restrict__ vp,
+                                   float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                                   int32_t n, int64_t block_bytes, int32_t num_blocks) {
+  const int64_t per = block_bytes / 16;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= per * n) return;
+  const int64_t pair = gid / per, c = gid % per;
+  const int32_t s = src[pair], d = dst[pair];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  const int64_t so = s * block_bytes + c * 16, dof = d * block_bytes + c * 16;
+  *reinterpret_cast<u32x4*>(kp + dof) = *reinterpret_cast<const u32x4*>(kp + so);
+  *reinterpret_cast<u32x4*>(vp + dof) = *reinterpret_cast<const u32x4*>(vp + so);
+  if (c == 0 && k_scale) {
+    k_scale[d] = k_scale[s];
+    v_scale[d] = v_scale[s];
+  }
+}
+
 // One workgroup per (logical page j, sequence b).
 template <typename T>
 __global__ void gather_kernel(const T* __restrict__ kp, const T* __restrict__ vp,
@@ -188,7 +281,7 @@ unsigned blocks_for(int64_t threads, int per_block) {
 
 hipError_t launch_write_kv(const pa_kv_pool& pool, const void* k_new, const void* v_new,
                            pa_dtype src, const int32_t* slots, int32_t n, uint32_t* amax_ws,
-                           hipStream_t st) {
+                           bool append, hipStream_t st) {
   const int Hkv = pool.num_kv_heads, D = pool.head_dim, NB = pool.num_blocks;
   if (pool.kv_dtype == PA_F32 || pool.kv_dtype == PA_BF16) {
     const int epc = pool.kv_dtype == PA_F32 ? 4 : 8;
@@ -208,22 +301,47 @@ hipError_t launch_write_kv(const pa_kv_pool& pool, const void* k_new, const void
   }
   fill_u32_kernel<<<blocks_for(2 * static_cast<int64_t>(NB), 256), 256, 0, st>>>(
       amax_ws, 2 * static_cast<int64_t>(NB), 0u);
+  uint32_t* min_off = nullptr;
+  if (append) {
+    min_off = amax_ws + 2 * static_cast<int64_t>(NB);
+    fill_u32_kernel<<<blocks_for(NB, 256), 256, 0, st>>>(min_off, NB, static_cast<uint32_t>(kPage));
+  }
   const int64_t threads = static_cast<int64_t>(n) * Hkv * (D / 8);
   uint8_t* kp = static_cast<uint8_t*>(pool.k);
   uint8_t* vp = static_cast<uint8_t*>(pool.v);
-  if (src == PA_F32) {
-    const float* kn = static_cast<const float*>(k_new);
-    const float* vn = static_cast<const float*>(v_new);
-    fp8_amax_kernel<float><<<n, 256, 0, st>>>(kn, vn, slots, Hkv, D, NB, amax_ws);
-    fp8_encode_kernel<float><<<blocks_for(threads, 256), 256, 0, st>>>(
-        kp, vp, pool.k_scale, pool.v_scale, kn, vn, slots, n, Hkv, D, NB, amax_ws);
-  } else {
-    const uint16_t* kn = static_cast<const uint16_t*>(k_new);
-    const uint16_t* vn = static_cast<const uint16_t*>(v_new);
-    fp8_amax_kernel<uint16_t><<<n, 256, 0, st>>>(kn, vn, slots, Hkv, D, NB, amax_ws);
-    fp8_encode_kernel<uint16_t><<<blocks_for(threads, 256), 256, 0, st>>>(
-        kp, vp, pool.k_scale, pool.v_scale, kn, vn, slots, n, Hkv, D, NB, amax_ws);
+  if (src == PA_F32)
+    fp8_amax_kernel<float><<<n, 256, 0, st>>>(static_cast<const float*>(k_new),
+                                              static_cast<const float*>(v_new), slots, Hkv, D,
+                                              NB, amax_ws, min_off);
+  else
+    fp8_amax_kernel<uint16_t><<<n, 256, 0, st>>>(static_cast<const uint16_t*>(k_new),
+                                                 static_cast<const uint16_t*>(v_new), slots, Hkv,
+                                                 D, NB, amax_ws, min_off);
+  if (append) {
+    fp8_existing_amax_kernel<<<n, 256, 0, st>>>(kp, vp, pool.k_scale, pool.v_scale, slots, Hkv,
+                                                D, NB, min_off, amax_ws);
+    fp8_requant_kernel<<<n, 256, 0, st>>>(kp, vp, pool.k_scale, pool.v_scale, slots, Hkv, D, NB,
+                                          min_off, amax_ws);
   }
+  if (src == PA_F32)
+    fp8_encode_kernel<float><<<blocks_for(threads, 256), 256, 0, st>>>(
+        kp, vp, pool.k_scale, pool.v_scale, static_cast<const float*>(k_new),
+        static_cast<const float*>(v_new), slots, n, Hkv, D, NB, amax_ws);
+  else
+    fp8_encode_kernel<uint16_t><<<blocks_for(threads, 256), 256, 0, st>>>(
+        kp, vp, pool.k_scale, pool.v_scale, static_cast<const uint16_t*>(k_new),
+        static_cast<const uint16_t*>(v_new), slots, n, Hkv, D, NB, amax_ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const pa_kv_pool& pool, const int32_t* src, const int32_t* dst,
+                              int32_t n, hipStream_t st) {
+  const int64_t es = pool.kv_dtype == PA_F32 ? 4 : (pool.kv_dtype == PA_BF16 ? 2 : 1);
+  const int64_t block_bytes = static_cast<int64_t>(pool.num_kv_heads) * kPage * pool.head_dim * es;
+  const bool fp8 = pool.kv_dtype == PA_FP8_E4M3;
+  copy_blocks_kernel<<<blocks_for(block_bytes / 16 * n, 256), 256, 0, st>>>(
+      static_cast<char*>(pool.k), static_cast<char*>(pool.v), fp8 ? pool.k_scale : nullptr,
+      fp8 ? pool.v_scale : nullptr, src, dst, n, block_bytes, pool.num_blocks);
   return hipGetLastError();
 }
 

@@ -91,7 +91,9 @@ __device__ __forceinline__ float sum_xor16(float x) {
 // Each returns hipSuccess or the launch error; arguments are already checked.
 hipError_t launch_write_kv(const pa_kv_pool& pool, const void* k_new, const void* v_new,
                            pa_dtype src, const int32_t* slots, int32_t n, uint32_t* amax_ws,
-                           hipStream_t st);
+                           bool append, hipStream_t st);
+hipError_t launch_copy_blocks(const pa_kv_pool& pool, const int32_t* src, const int32_t* dst,
+                              int32_t n, hipStream_t st);
 hipError_t launch_gather_kv(const pa_kv_pool& pool, const int32_t* bt, int32_t bt_stride,
                             const int32_t* ctx, const int32_t* cu_ctx, int32_t B,
                             int32_t max_ctx, void* k_out, void* v_out, hipStream_t st);

@@ -18,11 +18,15 @@ the attention mathematics):
 * ``attention`` -- the full score matrix S = scale * Q K^T, causal mask, a
                    two-pass safe softmax, O = P V and LSE = m + ln l, in f64.
 * ``fp8_e4m3``  -- the OCP E4M3FN codec from the format's bit definition.
+* ``blocks``    -- a plain model of block management: on-demand blocks, shared
+                   blocks with reference counts, copy on write before a
+                   sequence writes into a shared block (the PagedAttention
+                   section of the survey page).
 
 Every function is pinned by the ``-m "not gpu"`` tests in tests/test_oracle.py
 (brute force, closed forms, library special cases and invariants).
 """
-from . import fp8_e4m3, pool, attention  # noqa: F401
-from .pool import OraclePool, write_kv, gather_kv  # noqa: F401
+from . import fp8_e4m3, pool, attention, blocks  # noqa: F401
+from .pool import OraclePool, write_kv, append_kv, copy_blocks, gather_kv  # noqa: F401
 from .attention import (attention_two_pass, paged_attention, paged_attention_rows,  # noqa: F401
                         online_softmax_pages, lse_merge)

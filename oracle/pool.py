@@ -129,3 +129,59 @@ def gather_kv(pool: OraclePool, block_table_row, ctx_len: int, kv_head: int):
         K[j * BLOCK: j * BLOCK + n] = _decode(pool.k[p, kv_head, :n, :], pool.kv_dtype, ks)
         V[j * BLOCK: j * BLOCK + n] = _decode(pool.v[p, kv_head, :, :n].T, pool.kv_dtype, vs)
     return K, V
+
+
+def append_kv(pool: OraclePool, k_src: torch.Tensor, v_src: torch.Tensor,
+              slot_mapping: torch.Tensor) -> None:
+    """Append token t's K/V to slot_mapping[t], keeping the tokens a touched page
+    already holds: those at offsets below the lowest offset written to it here.
+
+    f32 / bf16 pools: the same copy as write_kv.  fp8 pools: per touched page,
+    the existing tokens' values as stored (code times the old scale, in float32)
+    and the new values share one new scale (amax over both, all heads, / 448)
+    and are all encoded with it, nearest even after clamping to +-448.
+    """
+    if pool.kv_dtype in ("f32", "bf16"):
+        write_kv(pool, k_src, v_src, slot_mapping)
+        return
+    slots = slot_mapping.numpy().astype(np.int64)
+    pages, offs = slots // BLOCK, slots % BLOCK
+    assert ((pages >= 0) & (pages < pool.num_blocks)).all()
+    kf, vf = _to_f32(k_src), _to_f32(v_src)                      # [n, Hkv, d]
+    table = fp8_e4m3.decode_table().astype(np.float32)
+    for p in np.unique(pages):
+        toks = np.nonzero(pages == p)[0]
+        m = int(offs[toks].min())                                  # existing: offsets < m
+        # K: page rows are tokens; V: page columns are tokens
+        old_k = table[pool.k[p, :, :m, :]] * np.float32(pool.k_scale[p]) if m else None
+        old_v = table[pool.v[p, :, :, :m]] * np.float32(pool.v_scale[p]) if m else None
+        new_k = kf[toks]                                           # [n_p, Hkv, d]
+        new_v = vf[toks]
+        # one quantisation over [existing; new] values of the page
+        k_all = new_k.reshape(-1) if old_k is None else np.concatenate(
+            [old_k.astype(np.float32).reshape(-1), new_k.reshape(-1)])
+        v_all = new_v.reshape(-1) if old_v is None else np.concatenate(
+            [old_v.astype(np.float32).reshape(-1), new_v.reshape(-1)])
+        k_codes, ks = _quantize_page(k_all)
+        v_codes, vs = _quantize_page(v_all)
+        pool.k_scale[p], pool.v_scale[p] = ks, vs
+        nk_old = 0 if old_k is None else old_k.size
+        nv_old = 0 if old_v is None else old_v.size
+        if m:
+            pool.k[p, :, :m, :] = k_codes[:nk_old].reshape(old_k.shape)
+            pool.v[p, :, :, :m] = v_codes[:nv_old].reshape(old_v.shape)
+        kn = k_codes[nk_old:].reshape(new_k.shape)
+        vn = v_codes[nv_old:].reshape(new_v.shape)
+        for j, t in enumerate(toks):
+            pool.k[p, :, offs[t], :] = kn[j]
+            pool.v[p, :, :, offs[t]] = vn[j]
+
+
+def copy_blocks(pool: OraclePool, src, dst) -> None:
+    """Block dst[i] becomes a copy of block src[i] (both pools, and fp8 scales)."""
+    for s, d in zip(list(src), list(dst)):
+        pool.k[d] = pool.k[s]
+        pool.v[d] = pool.v[s]
+        if pool.kv_dtype == "fp8":
+            pool.k_scale[d] = pool.k_scale[s]
+            pool.v_scale[d] = pool.v_scale[s]

@@ -161,5 +161,5 @@ def test_write_kv_checks():
     assert pa._write(p.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, -1, None, 0, None) == pa.PA_ERR_INVALID_ARG
     assert pa._write(p.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, 0, None, 0, None) == pa.PA_OK
     f = _FakePool(kv_dtype=pa.PA_FP8_E4M3)
-    assert pa._write_ws(f.c) == 2 * 4 * 8
+    assert pa._write_ws(f.c) == 3 * 4 * 8
     assert pa._write(f.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, 4, None, 0, None) == pa.PA_ERR_WORKSPACE

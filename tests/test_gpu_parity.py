@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from tests import harness as H
 
@@ -84,6 +85,74 @@ def test_gather_kv_bit_exact(kv_dtype):
             assert np.array_equal(kb[off + t], opool.k[p, :, t % 16, :])
             assert np.array_equal(vb[off + t], opool.v[p, :, :, t % 16])
         off += c
+
+
+# ------------------------------------------------------------ append path
+def _append_rounds(kv_dtype, src, D, seed):
+    """Three sequences; sequence 1 forks sequence 0's pages (its last page
+    partly filled and then shared); rounds of appends planned by the host
+    allocator, copied (copy on write) and appended on the device and in the
+    oracle.  Yields after every round."""
+    g = torch.Generator().manual_seed(seed)
+    NB, Hkv, W = 48, 2, 10
+    pool = pa.KVPool(NB, Hkv, D, kv_dtype)
+    opool = oracle.OraclePool(NB, Hkv, D, kv_dtype)
+    alloc = pa.BlockAllocator(NB)
+    bt = torch.full((3, W), -1, dtype=torch.int32)
+    cl = torch.zeros(3, dtype=torch.int32)
+    sdt = {"f32": torch.float32, "bf16": torch.bfloat16}[src]
+    scales = iter([1.0, 2.0, 0.5, 3.0, 1.0])
+    for r in ([37, 0, 5], "fork", [1, 1, 0], [0, 12, 16], [20, 3, 1], [1, 1, 1]):
+        if r == "fork":
+            bt[1], cl[1] = bt[0], cl[0]
+            for p in bt[0, :(int(cl[0]) + 15) // 16].tolist():
+                alloc.incref(p)
+            continue
+        slots, csrc, cdst = alloc.plan_append(bt, cl, r)
+        sc = next(scales)
+        k = (torch.randn(len(slots), Hkv, D, generator=g) * sc).to(sdt)
+        v = (torch.randn(len(slots), Hkv, D, generator=g) * sc).to(sdt)
+        if len(csrc):
+            pa.copy_blocks(pool, csrc.cuda(), cdst.cuda())
+            oracle.copy_blocks(opool, csrc.tolist(), cdst.tolist())
+        pa.append_kv(pool, k.cuda(), v.cuda(), slots.cuda())
+        oracle.append_kv(opool, k, v, slots)
+        yield pool, opool, bt, cl, len(csrc)
+
+
+@pytest.mark.parametrize("kv_dtype,src", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16"),
+                                          ("fp8", "f32")])
+def test_append_rounds_bit_exact(kv_dtype, src):
+    _log(f"append_kv rounds {kv_dtype} <- {src}")
+    copies = 0
+    for pool, opool, bt, cl, nc in _append_rounds(kv_dtype, src, 64, seed=71):
+        torch.cuda.synchronize()
+        copies += nc
+        assert np.array_equal(_bits(pool.k), opool.k)
+        assert np.array_equal(_bits(pool.v), opool.v)
+        if kv_dtype == "fp8":
+            assert np.array_equal(_bits(pool.k_scale), opool.k_scale.view(np.uint32))
+            assert np.array_equal(_bits(pool.v_scale), opool.v_scale.view(np.uint32))
+    assert copies == 1                                     # the shared partial page
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_decode_after_each_append_round(kv_dtype):
+    _log(f"decode after appends {kv_dtype}")
+    g = torch.Generator().manual_seed(72)
+    Hq, D = 4, 128
+    qd = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    scale = D ** -0.5
+    for pool, opool, bt, cl, _ in _append_rounds(kv_dtype, "f32" if kv_dtype == "f32" else "bf16",
+                                                 D, seed=73):
+        q = torch.randn(3, Hq, D, generator=g).to(qd)
+        o, lse = pa.decode(pool, q.cuda(), cl.cuda(), bt.cuda(), scale, max_ctx_len=bt.shape[1] * 16)
+        torch.cuda.synchronize()
+        ro, rl = oracle.paged_attention(opool, q, torch.arange(4), cl, bt, Hq, scale, True)
+        eo, el = H.max_err(o, lse, ro, rl)
+        tol = H.TOL["fp8" if kv_dtype == "fp8" else ("f32" if kv_dtype == "f32" else "bf16")]
+        _log(f"  ctx {cl.tolist()}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= tol and el <= tol, (cl.tolist(), eo, el)
 
 
 # ------------------------------------------------------------ decode parity
