@@ -1,6 +1,6 @@
 """Benchmark of the paged attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload headline|1..5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload headline|1..5|append] [--no-cpu-baseline]
     python bench.py --pmc-summary FETCH.csv WRITE.csv --copy-calib-mb N   (host only)
 
 One step runs every call of the selected workloads once, inputs already
@@ -172,6 +172,72 @@ def cpu_baseline(wls, budget_s: float):
     return out
 
 
+def bench_append(args):
+    """One decode step's KV append per batch: host planning (pa_plan_append),
+    the slot upload (through pinned memory), copies of shared pages (none: every sequence owns its
+    pages here) and pa_append_kv, on the batched decode batch (bf16 pool, 32
+    sequences) and the mixed batch's shapes (fp8 pool, 16 sequences of 1536
+    tokens, so every step re-quantises 16 partly filled pages).  Each step
+    appends one token to every sequence."""
+    import torch
+
+    import online_softmax_paged_amd as pa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    out = {"metric": "KV append per decode step (plan + copies + append_kv), 1 MI355X",
+           "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "vs_baseline": None, "scaling": "weak",
+           "data": "synthetic (seeded N(0,1) K/V)", "parts": []}
+    for wl in (workloads.batched_decode_bf16(), workloads.mixed_fp8()):
+        B, Hkv, D = len(wl.ctx_lens), wl.num_kv_heads, wl.head_dim
+        steps = args.warmup + args.steps
+        W = (max(wl.ctx_lens) + steps + 15) // 16
+        NB = sum((c + steps + 15) // 16 for c in wl.ctx_lens) + 8
+        pool = pa.KVPool(NB, Hkv, D, wl.kv_dtype, device=dev)
+        alloc = pa.BlockAllocator(NB)
+        bt = torch.full((B, W), -1, dtype=torch.int32)
+        cl = torch.zeros(B, dtype=torch.int32)
+        slots, _, _ = alloc.plan_append(bt, cl, list(wl.ctx_lens))
+        src_dt = torch.bfloat16
+        n0 = int(slots.numel())
+        g = torch.Generator().manual_seed(2024)
+        pa.write_kv(pool, torch.randn(n0, Hkv, D, generator=g).to(src_dt).to(dev),
+                    torch.randn(n0, Hkv, D, generator=g).to(src_dt).to(dev), slots.to(dev))
+        kn = torch.randn(steps, B, Hkv, D, generator=g).to(src_dt).to(dev)
+        vn = torch.randn(steps, B, Hkv, D, generator=g).to(src_dt).to(dev)
+        ws = torch.empty(max(1, pa.write_kv_workspace_bytes(pool)), dtype=torch.uint8, device=dev)
+        staged = torch.empty(B, dtype=torch.int32, pin_memory=True)   # slot upload staging
+        slots_dev = torch.empty(B, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        host_s, dev_ms = 0.0, 0.0
+        for i in range(steps):
+            t0 = time.perf_counter()
+            slots, csrc, cdst = alloc.plan_append(bt, cl, [1] * B)
+            staged.copy_(slots)
+            t1 = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if len(csrc):
+                pa.copy_blocks(pool, csrc.to(dev), cdst.to(dev))
+            slots_dev.copy_(staged, non_blocking=True)
+            pa.append_kv(pool, kn[i], vn[i], slots_dev, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                host_s += t1 - t0
+                dev_ms += e0.elapsed_time(e1)
+        out["parts"].append({"workload": wl.name, "kv_dtype": wl.kv_dtype, "sequences": B,
+                             "device_us": dev_ms * 1e3 / args.steps,
+                             "plan_us": host_s * 1e6 / args.steps})
+    out["value"] = sum(p["device_us"] + p["plan_us"] for p in out["parts"]) / len(out["parts"])
+    out["ms_per_step"] = out["value"] / 1e3
+    out["dtype"] = "bf16+bf16-src/fp8-kv"
+    out["config"] = {"workload": " + ".join(p["workload"] for p in out["parts"]) + " (append)"}
+    out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +279,9 @@ def main():
     import online_softmax_paged_amd as pa
     import workloads
 
+    if args.workload == "append":
+        bench_append(args)
+        return
     if args.workload == "headline":
         wls = [workloads.causal_prefill_bf16(), workloads.long_decode_bf16()]
     else:

@@ -49,9 +49,10 @@ __global__ void write_copy_kernel(T* __restrict__ kp, T* __restrict__ vp,
   for (int e = 0; e < EPC; ++e) vp[chunk_base + (c * EPC + e) * kPage + off] = vals[e];
 }
 
-__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
+// p[0, n0) = v0, p[n0, n) = v1.
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n0, int64_t n, uint32_t v0, uint32_t v1) {
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = value;
+  if (i < n) p[i] = i < n0 ? v0 : v1;
 }
 
 template <typename S>
@@ -163,57 +164,49 @@ __global__ void fp8_encode_kernel(uint8_t* __restrict__ kp, uint8_t* __restrict_
 }
 
 // Appending, pass 3: the token at the lowest offset written to its page leads
-// the page: it folds the page's existing values (offsets below it, all heads,
-// as stored: code * old scale) into the page's amax words.
-__global__ void fp8_existing_amax_kernel(const uint8_t* __restrict__ kp,
-                                         const uint8_t* __restrict__ vp,
-                                         const float* __restrict__ k_scale,
-                                         const float* __restrict__ v_scale,
-                                         const int32_t* __restrict__ slots, int32_t Hkv,
-                                         int32_t D, int32_t num_blocks,
-                                         const uint32_t* __restrict__ min_off,
-                                         uint32_t* __restrict__ amax_ws) {
+// the page.  The new tokens' amax is final (pass 2); the leader adds the
+// page's existing values (offsets below it, all heads, as stored: code * old
+// scale), stores the page's final amax for pass 4, and re-encodes the existing
+// codes with the new scale (the old scale is still in the scale arrays; pass
+// 4, which stores the new one, runs after this).
+__global__ __launch_bounds__(256) void fp8_requant_kernel(
+    uint8_t* __restrict__ kp, uint8_t* __restrict__ vp, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ slots, int32_t Hkv, int32_t D,
+    int32_t num_blocks, const uint32_t* __restrict__ min_off, uint32_t* __restrict__ amax_ws) {
   const int32_t slot = slots[blockIdx.x];
   const int32_t phys = slot >> 4, off = slot & 15;
   if (slot < 0 || phys >= num_blocks || static_cast<uint32_t>(off) != min_off[phys] || off == 0)
     return;
-  const float sk = k_scale[phys], sv = v_scale[phys];
+  const float sk_old = k_scale[phys], sv_old = v_scale[phys];
   const int64_t base = static_cast<int64_t>(phys) * Hkv * kPage * D;
   const int n = Hkv * off * D;  // existing values per pool
   float mk = 0.f, mv = 0.f;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int d = i % D, t = (i / D) % off, h = i / (D * off);
     const int64_t chunk = base + static_cast<int64_t>(h) * kPage * D;
-    mk = fmaxf(mk, fabsf(__builtin_amdgcn_cvt_f32_fp8(kp[chunk + t * D + d], 0) * sk));
-    mv = fmaxf(mv, fabsf(__builtin_amdgcn_cvt_f32_fp8(vp[chunk + d * kPage + t], 0) * sv));
+    mk = fmaxf(mk, fabsf(__builtin_amdgcn_cvt_f32_fp8(kp[chunk + t * D + d], 0) * sk_old));
+    mv = fmaxf(mv, fabsf(__builtin_amdgcn_cvt_f32_fp8(vp[chunk + d * kPage + t], 0) * sv_old));
   }
   for (int s = 32; s >= 1; s >>= 1) {
     mk = fmaxf(mk, __shfl_xor(mk, s));
     mv = fmaxf(mv, __shfl_xor(mv, s));
   }
+  __shared__ float red[2][4];
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    atomicMax(&amax_ws[phys], __float_as_uint(mk));
-    atomicMax(&amax_ws[num_blocks + phys], __float_as_uint(mv));
+    red[0][w] = mk;
+    red[1][w] = mv;
   }
-}
-
-// Appending, pass 4: the page leader re-encodes the page's existing codes with
-// the new scale (the old one is still in the scale arrays; the new tokens'
-// pass, which stores the new scale, runs after this one).
-__global__ void fp8_requant_kernel(uint8_t* __restrict__ kp, uint8_t* __restrict__ vp,
-                                   const float* __restrict__ k_scale,
-                                   const float* __restrict__ v_scale,
-                                   const int32_t* __restrict__ slots, int32_t Hkv, int32_t D,
-                                   int32_t num_blocks, const uint32_t* __restrict__ min_off,
-                                   const uint32_t* __restrict__ amax_ws) {
-  const int32_t slot = slots[blockIdx.x];
-  const int32_t phys = slot >> 4, off = slot & 15;
-  if (slot < 0 || phys >= num_blocks || static_cast<uint32_t>(off) != min_off[phys] || off == 0)
-    return;
-  const float sk_old = k_scale[phys], sv_old = v_scale[phys];
-  const float sk = fp8_scale_of(amax_ws[phys]), sv = fp8_scale_of(amax_ws[num_blocks + phys]);
-  const int64_t base = static_cast<int64_t>(phys) * Hkv * kPage * D;
-  const int n = Hkv * off * D;
+  __syncthreads();
+  mk = fmaxf(__uint_as_float(amax_ws[phys]), fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])));
+  mv = fmaxf(__uint_as_float(amax_ws[num_blocks + phys]),
+             fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])));
+  __syncthreads();  // every thread has read the new tokens' amax
+  if (threadIdx.x == 0) {
+    amax_ws[phys] = __float_as_uint(mk);
+    amax_ws[num_blocks + phys] = __float_as_uint(mv);
+  }
+  const float sk = fp8_scale_of(__float_as_uint(mk)), sv = fp8_scale_of(__float_as_uint(mv));
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int d = i % D, t = (i / D) % off, h = i / (D * off);
     const int64_t chunk = base + static_cast<int64_t>(h) * kPage * D;
@@ -299,13 +292,11 @@ hipError_t launch_write_kv(const pa_kv_pool& pool, const void* k_new, const void
     }
     return hipGetLastError();
   }
-  fill_u32_kernel<<<blocks_for(2 * static_cast<int64_t>(NB), 256), 256, 0, st>>>(
-      amax_ws, 2 * static_cast<int64_t>(NB), 0u);
-  uint32_t* min_off = nullptr;
-  if (append) {
-    min_off = amax_ws + 2 * static_cast<int64_t>(NB);
-    fill_u32_kernel<<<blocks_for(NB, 256), 256, 0, st>>>(min_off, NB, static_cast<uint32_t>(kPage));
-  }
+  // amax words (K then V) to 0 and, when appending, the lowest-offset words to 16
+  const int64_t words = (append ? 3 : 2) * static_cast<int64_t>(NB);
+  fill_u32_kernel<<<blocks_for(words, 256), 256, 0, st>>>(amax_ws, 2 * static_cast<int64_t>(NB),
+                                                          words, 0u, static_cast<uint32_t>(kPage));
+  uint32_t* min_off = append ? amax_ws + 2 * static_cast<int64_t>(NB) : nullptr;
   const int64_t threads = static_cast<int64_t>(n) * Hkv * (D / 8);
   uint8_t* kp = static_cast<uint8_t*>(pool.k);
   uint8_t* vp = static_cast<uint8_t*>(pool.v);
@@ -317,12 +308,9 @@ hipError_t launch_write_kv(const pa_kv_pool& pool, const void* k_new, const void
     fp8_amax_kernel<uint16_t><<<n, 256, 0, st>>>(static_cast<const uint16_t*>(k_new),
                                                  static_cast<const uint16_t*>(v_new), slots, Hkv,
                                                  D, NB, amax_ws, min_off);
-  if (append) {
-    fp8_existing_amax_kernel<<<n, 256, 0, st>>>(kp, vp, pool.k_scale, pool.v_scale, slots, Hkv,
-                                                D, NB, min_off, amax_ws);
+  if (append)
     fp8_requant_kernel<<<n, 256, 0, st>>>(kp, vp, pool.k_scale, pool.v_scale, slots, Hkv, D, NB,
                                           min_off, amax_ws);
-  }
   if (src == PA_F32)
     fp8_encode_kernel<float><<<blocks_for(threads, 256), 256, 0, st>>>(
         kp, vp, pool.k_scale, pool.v_scale, static_cast<const float*>(k_new),
