@@ -300,9 +300,14 @@ def main():
             o = torch.empty_like(q)
             lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
             if call.kind == "prefill":
-                fn = (lambda pool=pool, q=q, cu=cu, ctx=ctx, bt=bt, mq=mq, mc=mc, o=o, lse=lse, wl=wl, c=call:
+                B, Hq, D = len(call.q_lens), q.shape[1], q.shape[2]
+                S = pa.prefill_num_splits(B, wl.num_kv_heads, Hq, mq, mc)
+                ws = torch.empty(max(1, pa.prefill_workspace_bytes(B, mq, Hq, D, S)),
+                                 dtype=torch.uint8, device=dev)
+                fn = (lambda pool=pool, q=q, cu=cu, ctx=ctx, bt=bt, mq=mq, mc=mc, o=o, lse=lse, wl=wl,
+                      c=call, S=S, ws=ws:
                       pa.prefill(pool, q, cu, ctx, bt, wl.scale, causal=c.causal, max_q_len=mq,
-                                 max_ctx_len=mc, out=o, lse=lse))
+                                 max_ctx_len=mc, out=o, lse=lse, num_splits=S, workspace=ws))
             else:
                 B, Hq, D = q.shape
                 S = args.decode_splits or pa.decode_num_splits(B, wl.num_kv_heads, mc)

@@ -178,13 +178,27 @@ pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32
  * finite and > 0 (usually 1/sqrt(head_dim)).
  * Supported: q_dtype PA_F32 with an f32 pool; q_dtype PA_BF16 with a bf16 or
  * fp8 pool.  head_dim 64 or 128; num_q_heads / num_kv_heads in {1,2,4,8,16}.
- * q and o must be 16-byte aligned.
+ * q and o must be 16-byte aligned.  A sequence with q_len_b = 1 is a decode
+ * row, so one call can serve a mixed batch of chunked prefills and decodes.
+ * Key splits: each query tile's visible keys can be cut into num_splits
+ * contiguous ranges of 32-key tiles; each range gives a normalised partial
+ * output and logsumexp in the workspace, and a second pass merges them by
+ * their logsumexps (as pa_decode does).  num_splits: 0 = choose with
+ * pa_prefill_num_splits(), 1 = none (no workspace needed), at most 16; fp32
+ * pools always run with one.  workspace: device memory of at least
+ * pa_prefill_workspace_bytes(num_seqs, max_q_len, num_q_heads, head_dim,
+ * splits) bytes, 16-byte aligned, contents need not be initialised.
  */
+int32_t pa_prefill_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t num_q_heads,
+                              int32_t max_q_len, int32_t max_ctx_len);
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t num_splits);
 pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
                      float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
                      const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
                      int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
-                     float scale, int32_t causal, void* stream);
+                     float scale, int32_t causal, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ decode
  * One query token per sequence, at position ctx_len_b - 1 (it sees all

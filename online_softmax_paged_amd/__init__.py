@@ -53,7 +53,9 @@ _write = _sig("pa_write_kv", ctypes.c_int, [_P, _VP, _VP, ctypes.c_int, _VP, _I3
 _gather = _sig("pa_gather_kv", ctypes.c_int, [_P, _VP, _I32, _VP, _VP, _I32, _I32, _VP, _VP, _VP])
 _prefill = _sig("pa_prefill", ctypes.c_int,
                 [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
-                 _F, _I32, _VP])
+                 _F, _I32, _I32, _VP, _SZ, _VP])
+_pre_splits = _sig("pa_prefill_num_splits", _I32, [_I32, _I32, _I32, _I32, _I32])
+_pre_ws = _sig("pa_prefill_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32, _I32])
 _num_splits = _sig("pa_decode_num_splits", _I32, [_I32, _I32, _I32])
 _dec_ws = _sig("pa_decode_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
 _decode = _sig("pa_decode", ctypes.c_int,
@@ -75,7 +77,8 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_gather_kv", "pa_prefill", "pa_decode_num_splits", "pa_decode_workspace_bytes",
             "pa_decode", "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_block",
             "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks",
-            "pa_append_kv", "pa_copy_blocks", "pa_plan_append"]
+            "pa_append_kv", "pa_copy_blocks", "pa_plan_append", "pa_prefill_num_splits",
+            "pa_prefill_workspace_bytes"]
 
 
 class PAError(RuntimeError):
@@ -218,9 +221,20 @@ def _validate(pool: KVPool, ctx_lens, block_table, q_lens=None):
             raise ValueError(f"sequence {b}: q_len {q_lens[b]} not in [1, {c}]")
 
 
+def prefill_num_splits(num_seqs: int, num_kv_heads: int, num_q_heads: int, max_q_len: int,
+                       max_ctx_len: int) -> int:
+    return int(_pre_splits(num_seqs, num_kv_heads, num_q_heads, max_q_len, max_ctx_len))
+
+
+def prefill_workspace_bytes(num_seqs: int, max_q_len: int, num_q_heads: int, head_dim: int,
+                            num_splits: int) -> int:
+    return int(_pre_ws(num_seqs, max_q_len, num_q_heads, head_dim, num_splits))
+
+
 def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, scale: float,
             causal: bool = True, max_q_len: int | None = None, max_ctx_len: int | None = None,
             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+            num_splits: int = 0, workspace: torch.Tensor | None = None,
             validate: bool = False, stream=None):
     """Attention of query chunks (the last q_len_b positions of each sequence).
     Returns (o, lse): o like q, lse float32 [T, Hq]."""
@@ -234,13 +248,22 @@ def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, sca
             max_ctx_len = int(ctx_lens.max().item()) if B else 0
         if validate:
             _validate(pool, ctx_lens, block_table, q_lens)
-    T, Hq, _ = q.shape
+    T, Hq, D = q.shape
+    if num_splits == 0:
+        num_splits = prefill_num_splits(B, pool.num_kv_heads, Hq, max_q_len, max_ctx_len)
+    if pool.kv_dtype == "f32":
+        num_splits = 1
+    need = prefill_workspace_bytes(B, max_q_len, Hq, D, num_splits)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
     _check(_prefill(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(cu_q_lens),
                     _ptr(ctx_lens), _ptr(block_table), block_table.shape[1], B, Hq, max_q_len,
-                    max_ctx_len, scale, 1 if causal else 0, _stream(stream)), "pa_prefill")
+                    max_ctx_len, scale, 1 if causal else 0, num_splits,
+                    _ptr(workspace) if need else None, workspace.numel() if need else 0,
+                    _stream(stream)), "pa_prefill")
     return o, lse
 
 

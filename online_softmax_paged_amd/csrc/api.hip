@@ -91,7 +91,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 1; }
+int32_t pa_abi_version(void) { return 2; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
@@ -166,21 +166,70 @@ pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32
                                    max_ctx_len, k_out, v_out, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_prefill_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t num_q_heads,
+                              int32_t max_q_len, int32_t max_ctx_len) {
+  if (num_seqs < 1 || num_kv_heads < 1 || num_q_heads < num_kv_heads || max_q_len < 1 ||
+      max_ctx_len < 1)
+    return 1;
+  // Query tiles hold 128 rows (positions x the group's heads).  Split the keys
+  // only when the tiles alone give fewer than 512 workgroups (two per compute
+  // unit), keeping at least 8 key tiles of 32 per split.  With enough tiles
+  // the kernel is bound by each unit's throughput, not by the length of a
+  // tile's key loop (8 x 256 queries over 1536 fp8 keys: 85 us unsplit, 85 us
+  // with 2 splits plus 26 us of merge); with few it is not (1 x 256 queries
+  // over 8192 bf16 keys: 214 us unsplit, 70 us with 4 splits, 60 us with 8).
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t tq = G >= 128 ? 1 : 128 / G;
+  const int64_t tiles = (max_q_len + tq - 1) / tq;
+  const int64_t wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * tiles;
+  int64_t s = (512 + wgs - 1) / wgs;
+  const int64_t by_keys = (max_ctx_len + 32 * 8 - 1) / (32 * 8);
+  if (s > by_keys) s = by_keys;
+  if (s > 16) s = 16;
+  return static_cast<int32_t>(s < 1 ? 1 : s);
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t num_splits) {
+  if (num_seqs < 1 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1 || num_splits <= 1)
+    return 0;
+  const size_t rows = static_cast<size_t>(num_splits) * num_seqs * max_q_len * num_q_heads;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return o_bytes + rows * sizeof(float);
+}
+
 pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
                      float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
                      const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
                      int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
-                     float scale, int32_t causal, void* stream) {
+                     float scale, int32_t causal, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (num_seqs == 0 && pool) return check_pool(pool);
   pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
                            num_q_heads, max_ctx_len, scale);
   if (s != PA_OK) return s;
   if (!cu_q_lens || max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 16) return PA_ERR_INVALID_ARG;
+  if (num_splits == 0)
+    num_splits = pa_prefill_num_splits(num_seqs, pool->num_kv_heads, num_q_heads, max_q_len,
+                                       max_ctx_len);
+  if (pool->kv_dtype == PA_F32) num_splits = 1;  // the fp32 kernel does not split keys
   AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
                          num_q_heads, max_ctx_len, scale);
   a.cu_q_lens = cu_q_lens;
   a.max_q_len = max_q_len;
   a.causal = causal ? 1 : 0;
+  a.num_splits = num_splits;
+  if (num_splits > 1) {
+    const size_t need = pa_prefill_workspace_bytes(num_seqs, max_q_len, num_q_heads,
+                                                   pool->head_dim, num_splits);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+    const size_t rows = static_cast<size_t>(num_splits) * num_seqs * max_q_len * num_q_heads;
+    const size_t o_bytes = (rows * pool->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  }
   return launched(launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -215,6 +215,45 @@ __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm
   }
 }
 
+// Epilogue of one lane (query row qrow, its half of the features): with one
+// key split, the output row (bf16) and its logsumexp; with several, this
+// split's normalised fp32 partial row and logsumexp in the workspace, at
+// ((split * num_seqs + b) * max_q_len + token) * Hq + head.
+template <int D>
+__device__ __forceinline__ void write_rows(const AttnArgs& a, const f32x16 (&acc)[D / 32],
+                                           float m, float l, int64_t qrow, int b, int tt,
+                                           int h, int split, int half) {
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  const float lse = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+  if (a.num_splits == 1) {
+    uint16_t* op = static_cast<uint16_t*>(a.o) + qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w.x = pack_bf16x2(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv);
+        w.y = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + db * 32 + 8 * j + 4 * half) = w;
+      }
+    if (half == 0 && a.lse) a.lse[qrow] = lse;
+    return;
+  }
+  const int64_t prow =
+      ((static_cast<int64_t>(split) * a.num_seqs + b) * a.max_q_len + tt) * a.num_q_heads + h;
+  float* op = a.ws_o + prow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 w = {acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv,
+                       acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv};
+      *reinterpret_cast<f32x4*>(op + db * 32 + 8 * j + 4 * half) = w;
+    }
+  if (half == 0) a.ws_lse[prow] = lse;
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(AttnArgs a, int n_tiles) {
   __shared__ Smem<D> sm;
@@ -223,7 +262,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y);
+  const int S = a.num_splits;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y) / S;
+  const int split = static_cast<int>(blockIdx.y) % S;
   const int TQ = kRows / G;
 
   const int q0 = a.cu_q_lens[b];
@@ -236,7 +277,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int t_last = min(t0 + TQ, qlen) - 1;  // last token of this tile
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   if (kmax <= 0) return;                      // inconsistent lengths: nothing visible
-  const int n_kt = (kmax + kKeys - 1) / kKeys;
+  const int n_kt_all = (kmax + kKeys - 1) / kKeys;
+  // this split's key tiles [kt_begin, n_kt)
+  const int per_split = (n_kt_all + S - 1) / S;
+  const int kt_begin = split * per_split;
+  const int n_kt = min(n_kt_all, kt_begin + per_split);
   const int n_pages = (ctx + kPage - 1) / kPage;
   // Tiles whose keys are all visible to every row need no mask.
   const int first_pos = pos_base + t0;
@@ -270,16 +315,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  TilePages cur = pages_of<FP8>(a, bt, 0, n_pages);
-  TilePages nxt = pages_of<FP8>(a, bt, 1, n_pages);
+  TilePages cur = pages_of<FP8>(a, bt, kt_begin, n_pages);
+  TilePages nxt = pages_of<FP8>(a, bt, kt_begin + 1, n_pages);
   Stage<D, FP8> st;
-  stage_load<D, FP8>(st, a, g, cur, tid);
-  stage_store<D, FP8>(st, sm, 0, 0, ctx, cur, tid);
+  if (kt_begin < n_kt) {
+    stage_load<D, FP8>(st, a, g, cur, tid);
+    stage_store<D, FP8>(st, sm, 0, kt_begin, ctx, cur, tid);
+  }
   __syncthreads();
 
   constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt_begin; kt < n_kt; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
     const TilePages nn = pages_of<FP8>(a, bt, kt + 2, n_pages);
     if (kt + 1 < n_kt) stage_load<D, FP8>(st, a, g, nxt, tid);
 
@@ -359,19 +406,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 
   l = sum_xor32(l);
   if (!row_ok) return;
-  const bool empty = !(l > 0.f);
-  const float inv = empty ? 0.f : 1.f / l;
-  uint16_t* op = static_cast<uint16_t*>(a.o) + qrow * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x2 w;
-      w.x = pack_bf16x2(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv);
-      w.y = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + db * 32 + 8 * j + 4 * half) = w;
-    }
-  if (half == 0 && a.lse) a.lse[qrow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+  write_rows<D>(a, acc, m, l, qrow, b, tt, g * G + hg, split, half);
 }
 
 // ---------------------------------------------------------------------------
@@ -550,18 +585,21 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   // over the dies, die k takes pairs k*P .. k*P+P-1 and runs them two at a
   // time (about 4 MiB of K/V in flight, the size of its L2), longest query
   // tiles first across both pairs, so every die ends on short tiles.
-  const int n_bg = gridDim.x;
+  // (With key splits, the task index along y is tile-from-end * S + split,
+  // so a tile's splits stay together.)
+  const int S = a.num_splits;
+  const int n_bg = gridDim.x, n_y = gridDim.y;  // n_y = n_tiles * S
   const int lin = blockIdx.y * n_bg + blockIdx.x;
-  int bg = blockIdx.x, tile_from_end = blockIdx.y;
+  int bg = blockIdx.x, y = blockIdx.y;
   if (n_bg % 8 == 0) {
     const int P = n_bg / 8, GP = (P % 2 == 0) ? 2 : 1;
-    const int j = lin / 8, per_group = GP * n_tiles;
+    const int j = lin / 8, per_group = GP * n_y;
     const int grp = j / per_group, i = j % per_group;
     bg = (lin % 8) * P + grp * GP + i % GP;
-    tile_from_end = i / GP;
+    y = i / GP;
   }
   const int b = bg / Hkv, g = bg % Hkv;
-  const int tile = n_tiles - 1 - tile_from_end;
+  const int tile = n_tiles - 1 - y / S, split = y % S;
   constexpr int ROWS = 32 * NW;   // query rows per workgroup
   const int TQ = ROWS / G;
   constexpr int STAGE = DmaSmem<D>::STAGE;
@@ -585,7 +623,11 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   const int t_last = min(t0 + TQ, qlen) - 1;
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   if (kmax <= 0) return;
-  const int n_kt = (kmax + kKeys - 1) / kKeys;
+  const int n_kt_all = (kmax + kKeys - 1) / kKeys;
+  // this split's key tiles [kt_begin, n_kt)
+  const int per_split = (n_kt_all + S - 1) / S;
+  const int kt_begin = split * per_split;
+  const int n_kt = min(n_kt_all, kt_begin + per_split);
   const int n_pages = (ctx + kPage - 1) / kPage;
   const int first_pos = pos_base + t0;
   const int n_full = a.causal ? max(0, min((first_pos + 1) / kKeys, ctx / kKeys))
@@ -619,8 +661,10 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     return check_pages(a, r, t, n_pages);
   };
   const uint32_t lds0 = lds_address(sm.buf);
-  dma_tile<D, NW>(a, g, tile_pages(0), 0, ctx, lds0, plan);
-  dma_tile<D, NW>(a, g, tile_pages(1), 1, ctx, lds0 + STAGE, plan);
+  if (kt_begin < n_kt) {  // uniform; an empty split moves nothing
+    dma_tile<D, NW>(a, g, tile_pages(kt_begin), kt_begin, ctx, lds0, plan);
+    dma_tile<D, NW>(a, g, tile_pages(kt_begin + 1), kt_begin + 1, ctx, lds0 + STAGE, plan);
+  }
 
   bf16x8 qf[D / 16];
   {
@@ -644,7 +688,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
 
   // stage of tile kt and of tile kt + 2 (three stages in rotation)
   int st_cur = 0, st_pre = 2;
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = kt_begin; kt < n_kt; ++kt) {
     char* stg = sm.buf + st_cur * STAGE;
     if (kt == tail_tile) {
       // zero V^T slots of tokens at or past the context end in this stage
@@ -735,21 +779,10 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     __syncthreads();
   }
 
+  wait_vmcnt<0>();  // no DMA of this workgroup outlives it
   l = sum_xor32(l);
   if (!row_ok) return;
-  const bool empty = !(l > 0.f);
-  const float inv = empty ? 0.f : 1.f / l;
-  uint16_t* op = static_cast<uint16_t*>(a.o) + qrow * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x2 w;
-      w.x = pack_bf16x2(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv);
-      w.y = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + db * 32 + 8 * j + 4 * half) = w;
-    }
-  if (half == 0 && a.lse) a.lse[qrow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+  write_rows<D>(a, acc, m, l, qrow, b, tt, g * G + hg, split, half);
 }
 
 // fp32 pools: one wave per (query row, query head), 64 keys per step (see
@@ -789,6 +822,43 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
   if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
 }
 
+// Merge of the key splits of every query row: the logsumexp-weighted sum of
+// its S normalised partial rows (one wave per (sequence, token, head); empty
+// splits carry lse = -inf and weight 0).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int Hq = a.num_q_heads, S = a.num_splits;
+  const int64_t per_seq = static_cast<int64_t>(a.max_q_len) * Hq;
+  const int64_t stride = per_seq * a.num_seqs;  // partial rows per split
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (r >= stride) return;
+  const int b = static_cast<int>(r / per_seq);
+  const int i = static_cast<int>((r % per_seq) / Hq), h = static_cast<int>(r % Hq);
+  const int q0 = a.cu_q_lens[b];
+  if (i >= a.cu_q_lens[b + 1] - q0) return;
+  float M = -INFINITY;
+  for (int t = 0; t < S; ++t) M = fmaxf(M, a.ws_lse[t * stride + r]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  constexpr int NPL = D / 64;
+  float acc[NPL] = {};
+  float W = 0.f;
+  for (int t = 0; t < S; ++t) {
+    const float lt = a.ws_lse[t * stride + r];
+    const float w = lt == -INFINITY ? 0.f : fast_exp2((lt - Mu) * kLog2e);
+    W += w;
+    const float* op = a.ws_o + (t * stride + r) * D + lane;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[j] += w * op[64 * j];
+  }
+  const bool empty = !(W > 0.f);
+  const int64_t row = static_cast<int64_t>(q0 + i) * Hq + h;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j)
+    static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] = to_bf16_bits(empty ? 0.f : acc[j] / W);
+  if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : M + __logf(W);
+}
+
 template <int D>
 hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
   if (a.kv_dtype == PA_F32) {
@@ -803,11 +873,15 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = PA_PREFILL_WAVES;
   const int TQ = (a.kv_dtype == PA_BF16 ? 32 * NW : kRows) / G;
   const int n_tiles = (a.max_q_len + TQ - 1) / TQ;
-  const dim3 grid(a.num_seqs * a.num_kv_heads, n_tiles);
+  const dim3 grid(a.num_seqs * a.num_kv_heads, n_tiles * a.num_splits);
   if (a.kv_dtype == PA_FP8_E4M3)
     prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
   else
     prefill_dma_kernel<D, NW><<<grid, 64 * NW, 0, st>>>(a, n_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.max_q_len * a.num_q_heads;
+  prefill_merge_kernel<D><<<static_cast<unsigned>((rows + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

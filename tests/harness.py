@@ -48,7 +48,7 @@ class DeviceCall:
         if self.kind == "prefill":
             return pa.prefill(pool, self.q, self.cu_q_lens, self.ctx_lens, self.block_table,
                               self.scale, causal=self.causal, max_q_len=self.max_q_len,
-                              max_ctx_len=self.max_ctx_len, **kw)
+                              max_ctx_len=self.max_ctx_len, num_splits=num_splits, **kw)
         return pa.decode(pool, self.q, self.ctx_lens, self.block_table, self.scale,
                          max_ctx_len=self.max_ctx_len, num_splits=num_splits, **kw)
 

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -96,11 +96,12 @@ class _FakePool:
 
 def _prefill(pool, **kw):
     a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, cu=0x8000, ctx=0x9000,
-             bt=0xa000, stride=4, B=2, Hq=8, max_q=64, max_ctx=64, scale=0.1, causal=1)
+             bt=0xa000, stride=4, B=2, Hq=8, max_q=64, max_ctx=64, scale=0.1, causal=1,
+             splits=1, ws=0, ws_bytes=0)
     a.update(kw)
     return pa._prefill(pool.c, a["q"], a["q_dtype"], a["o"], a["lse"], a["cu"], a["ctx"], a["bt"],
                        a["stride"], a["B"], a["Hq"], a["max_q"], a["max_ctx"], a["scale"],
-                       a["causal"], None)
+                       a["causal"], a["splits"], a["ws"], a["ws_bytes"], None)
 
 
 def _decode(pool, **kw):
@@ -145,6 +146,21 @@ def test_decode_workspace_checks():
     assert _decode(_FakePool(), ws=0x10000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
     assert _decode(_FakePool(), ws=0x10008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG
     assert _decode(_FakePool(), splits=-1) == pa.PA_ERR_INVALID_ARG
+
+
+def test_prefill_split_checks_and_heuristic():
+    need = pa.prefill_workspace_bytes(2, 64, 8, 128, 3)
+    assert need >= 3 * 2 * 64 * 8 * (128 + 1) * 4
+    assert pa.prefill_workspace_bytes(2, 64, 8, 128, 1) == 0
+    assert _prefill(_FakePool(), splits=3, ws=0) == pa.PA_ERR_WORKSPACE
+    assert _prefill(_FakePool(), splits=3, ws=0x10000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
+    assert _prefill(_FakePool(), splits=3, ws=0x10008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG
+    assert _prefill(_FakePool(), splits=17) == pa.PA_ERR_INVALID_ARG
+    # many query tiles: no split; few query tiles over long contexts: split
+    assert pa.prefill_num_splits(4, 8, 32, 4096, 4096) == 1
+    assert pa.prefill_num_splits(8, 8, 32, 256, 1536) == 1
+    assert pa.prefill_num_splits(1, 8, 32, 256, 8192) == 8
+    assert pa.prefill_num_splits(1, 1, 1, 10, 100) == 1
 
 
 def test_decode_split_heuristic():

@@ -211,6 +211,45 @@ def _named(k):
     return wl, H.oracle_pool(wl)
 
 
+PREFILL_SPLIT_CASES = [
+    # kv, D, Hq, Hkv, ctx_lens, q_lens, splits
+    ("bf16", 128, 8, 2, (700, 300), (45, 300), 2),
+    ("bf16", 128, 8, 2, (700, 300), (45, 300), 3),
+    ("bf16", 64, 4, 2, (333,), None, 3),
+    ("bf16", 128, 8, 2, (100, 37), None, 5),        # more splits than key tiles: empty ranges
+    ("fp8", 128, 8, 2, (400, 60), (256, 60), 2),
+    ("fp8", 128, 16, 2, (1000, 520), (256, 1), 4),
+]
+
+
+@pytest.mark.parametrize("kv,D,Hq,Hkv,ctx,ql,splits", PREFILL_SPLIT_CASES)
+def test_prefill_key_splits(kv, D, Hq, Hkv, ctx, ql, splits):
+    _log(f"prefill splits={splits} kv={kv} D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} q={ql}")
+    wl = workloads.small("prefill", kv_dtype=kv, q_dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, ctx_lens=ctx, q_lens=ql, seed=80 + splits)
+    _check_call(wl, wl.calls[0], H.device_pool(wl), H.oracle_pool(wl), num_splits=splits)
+
+
+def test_mixed_batch_in_one_prefill_call():
+    """Chunked prefills and q_len = 1 decode rows of one batch in a single
+    call (with and without key splits) match the oracle and the decode path."""
+    _log("mixed prefill + decode rows in one call")
+    wl = workloads.small("prefill", kv_dtype="fp8", q_dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, ctx_lens=(600, 300, 900, 45), q_lens=(128, 1, 1, 45), seed=85)
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    for splits in (1, 3, 0):
+        o, lse = _check_call(wl, wl.calls[0], pool, opool, num_splits=splits)
+    # the decode rows equal pa_decode on the same sequences
+    call = wl.calls[0]
+    sel = torch.tensor([1, 2])
+    q_dec = call.q[call.cu_q_lens[1:3].long()].cuda()
+    od, ld = pa.decode(pool, q_dec, call.ctx_lens[sel].cuda(), call.block_table[sel].cuda(),
+                       wl.scale, max_ctx_len=900, num_splits=1)
+    rows = call.cu_q_lens[1:3].long().cuda()
+    assert (o[rows].float() - od.float()).abs().max() <= 2 * H.TOL["fp8"]
+    assert (lse[rows] - ld).abs().max() <= 1e-3
+
+
 @pytest.mark.parametrize("k", [1, 2, 4, 5])
 def test_named_workload_full(k):
     _log(f"named workload {k}")
