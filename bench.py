@@ -238,6 +238,54 @@ def bench_append(args):
     print(json.dumps(out), flush=True)
 
 
+def one_call_timings(pa, wl, pool, dev, args, scratch):
+    """The workload's calls (chunks and decode rows) as ONE varlen call, timed
+    two ways after the main loop: pa_prefill, and pa_prefill_shared_prefix
+    (prefix attended once by all queries packed together).  Reported beside
+    the step; the step itself keeps its separate calls."""
+    import torch
+    import workloads
+    call = workloads.one_call(wl)
+    q = call.q.to(dev)
+    cu, ctx, bt = call.cu_q_lens.to(dev), call.ctx_lens.to(dev), call.block_table.to(dev)
+    mq, mc = max(call.q_lens), int(call.ctx_lens.max())
+    B, (T, Hq, D) = len(call.q_lens), q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    S = pa.prefill_num_splits(B, wl.num_kv_heads, Hq, mq, mc)
+    ws = torch.empty(max(1, pa.prefill_workspace_bytes(B, mq, Hq, D, S)), dtype=torch.uint8,
+                     device=dev)
+    sp, ss = pa.shared_prefix_num_splits(B, wl.num_kv_heads, Hq, mq, mc, wl.shared_prefix, T)
+    ws2 = torch.empty(pa.shared_prefix_workspace_bytes(T, Hq, D, sp + ss), dtype=torch.uint8,
+                      device=dev)
+    fns = {
+        "prefill": lambda: pa.prefill(pool, q, cu, ctx, bt, wl.scale, causal=call.causal,
+                                      max_q_len=mq, max_ctx_len=mc, out=o, lse=lse,
+                                      num_splits=S, workspace=ws),
+        "shared_prefix": lambda: pa.prefill_shared_prefix(
+            pool, q, cu, ctx, bt, wl.scale, wl.shared_prefix, causal=call.causal, max_q_len=mq,
+            max_ctx_len=mc, out=o, lse=lse, prefix_splits=sp, suffix_splits=ss, workspace=ws2),
+    }
+    out = {"workload": wl.name, "flops": prefill_flops(call, wl.head_dim, wl.num_q_heads),
+           "splits": {"prefill": S, "shared_prefix": [sp, ss]}}
+    for name, fn in fns.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(args.steps):
+            if scratch is not None:
+                scratch.sum(dtype=torch.int64)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        out[name + "_ms"] = tot / args.steps
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,9 +338,11 @@ def main():
     torch.cuda.set_device(dev)
 
     launches = []   # (kind, wl, fn)
+    pools = {}
     for wl in wls:
         pool = pa.KVPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, device=dev)
         pa.write_kv(pool, wl.k_src.to(dev), wl.v_src.to(dev), wl.slot_mapping.to(dev))
+        pools[wl.name] = pool
         for call in wl.calls:
             q = call.q.to(dev)
             cu, ctx, bt = call.cu_q_lens.to(dev), call.ctx_lens.to(dev), call.block_table.to(dev)
@@ -403,6 +453,9 @@ def main():
         result["decode"] = {"value": sum(x["kv_bytes"] for x in dec) / (sum(x["ms"] for x in dec) * 1e-3) / 1e9,
                             "unit": "GB/s", "frac_hbm_peak": None}
         result["decode"]["frac_hbm_peak"] = result["decode"]["value"] / PEAK_HBM_GBPS
+    for wl in wls:
+        if wl.shared_prefix and len(wl.calls) > 1:
+            parts["one_call"] = one_call_timings(pa, wl, pools[wl.name], dev, args, scratch)
     result["parts"] = parts
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wls, args.cpu_budget)

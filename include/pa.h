@@ -200,6 +200,56 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
                      float scale, int32_t causal, int32_t num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ shared prefix
+ * pa_prefill for a batch whose sequences all begin with the same prefix_len
+ * tokens held in the same physical blocks (reference-counted sharing of a
+ * common prompt's blocks: the survey page, section 3, "core principle").  The
+ * result is the same attention as pa_prefill with the same arguments; only
+ * the work is arranged differently:
+ *   1. all num_q_tokens query tokens of the batch, packed into one sequence,
+ *      attend the prefix keys 0..prefix_len-1 once per KV head (no mask: every
+ *      query lies past the prefix), read through block-table row 0;
+ *   2. each sequence's queries attend its own keys prefix_len..ctx_len_b-1
+ *      (causal as requested; when max_q_len is 1 this pass is pa_decode's
+ *      split pass over the pages past the prefix);
+ *   3. the normalised partials of both passes are merged by their logsumexps
+ *      (the combination of partial softmax statistics of the "core modules"
+ *      chapter, section 2.1).
+ * So a decode row's share of the prefix is multiplied in a matrix tile with
+ * the other sequences' rows instead of one sequence at a time.
+ * Arguments as pa_prefill, plus:
+ *   prefix_len   : a multiple of 16, >= 16, and prefix_len + max_q_len <=
+ *                  max_ctx_len (checked).
+ *   num_q_tokens : cu_q_lens[num_seqs], the rows of q and o; 1 <= num_q_tokens
+ *                  <= num_seqs * max_q_len (checked).  Rows of a sequence past
+ *                  num_q_tokens are not written.
+ *   prefix_splits, suffix_splits : key splits of passes 1 and 2, 0 = choose
+ *                  with pa_shared_prefix_num_splits(), at most 64 each.
+ *   workspace    : at least pa_shared_prefix_workspace_bytes(num_q_tokens,
+ *                  num_q_heads, head_dim, prefix_splits + suffix_splits) bytes
+ *                  of device memory, 16-byte aligned (always needed).
+ * Device-resident contract (not checked): for every b, block_table[b][j] ==
+ * block_table[0][j] for j < prefix_len / 16, and ctx_len_b - q_len_b >=
+ * prefix_len (no query inside the prefix).  If it does not hold the result is
+ * unspecified, but nothing outside the documented buffers is touched.
+ * Supported: bf16 and fp8 pools (PA_ERR_UNSUPPORTED for fp32 pools).
+ */
+pa_status pa_shared_prefix_num_splits(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t num_q_heads, int32_t max_q_len,
+                                      int32_t max_ctx_len, int32_t prefix_len,
+                                      int32_t num_q_tokens, int32_t* prefix_splits,
+                                      int32_t* suffix_splits);
+size_t pa_shared_prefix_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads,
+                                        int32_t head_dim, int32_t total_splits);
+pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype,
+                                   void* o, float* lse, const int32_t* cu_q_lens,
+                                   const int32_t* ctx_lens, const int32_t* block_table,
+                                   int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_q_len, int32_t max_ctx_len, float scale,
+                                   int32_t causal, int32_t prefix_len, int32_t num_q_tokens,
+                                   int32_t prefix_splits, int32_t suffix_splits,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ decode
  * One query token per sequence, at position ctx_len_b - 1 (it sees all
  * ctx_len_b cached keys).  Split-KV: each sequence's pages are cut into

@@ -56,6 +56,12 @@ _prefill = _sig("pa_prefill", ctypes.c_int,
                  _F, _I32, _I32, _VP, _SZ, _VP])
 _pre_splits = _sig("pa_prefill_num_splits", _I32, [_I32, _I32, _I32, _I32, _I32])
 _pre_ws = _sig("pa_prefill_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32, _I32])
+_sp_splits = _sig("pa_shared_prefix_num_splits", ctypes.c_int,
+                  [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP])
+_sp_ws = _sig("pa_shared_prefix_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
+_prefill_sp = _sig("pa_prefill_shared_prefix", ctypes.c_int,
+                   [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                    _F, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP])
 _num_splits = _sig("pa_decode_num_splits", _I32, [_I32, _I32, _I32])
 _dec_ws = _sig("pa_decode_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
 _decode = _sig("pa_decode", ctypes.c_int,
@@ -78,7 +84,8 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_decode", "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_block",
             "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks",
             "pa_append_kv", "pa_copy_blocks", "pa_plan_append", "pa_prefill_num_splits",
-            "pa_prefill_workspace_bytes"]
+            "pa_prefill_workspace_bytes", "pa_shared_prefix_num_splits",
+            "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix"]
 
 
 class PAError(RuntimeError):
@@ -264,6 +271,77 @@ def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, sca
                     max_ctx_len, scale, 1 if causal else 0, num_splits,
                     _ptr(workspace) if need else None, workspace.numel() if need else 0,
                     _stream(stream)), "pa_prefill")
+    return o, lse
+
+
+def shared_prefix_num_splits(num_seqs: int, num_kv_heads: int, num_q_heads: int,
+                             max_q_len: int, max_ctx_len: int, prefix_len: int,
+                             num_q_tokens: int) -> tuple[int, int]:
+    """Key splits (prefix pass, suffix pass) that prefill_shared_prefix picks."""
+    p, s = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_sp_splits(num_seqs, num_kv_heads, num_q_heads, max_q_len, max_ctx_len, prefix_len,
+                      num_q_tokens, ctypes.addressof(p), ctypes.addressof(s)),
+           "pa_shared_prefix_num_splits")
+    return p.value, s.value
+
+
+def shared_prefix_workspace_bytes(num_q_tokens: int, num_q_heads: int, head_dim: int,
+                                  total_splits: int) -> int:
+    return int(_sp_ws(num_q_tokens, num_q_heads, head_dim, total_splits))
+
+
+def prefill_shared_prefix(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table,
+                          scale: float, prefix_len: int, causal: bool = True,
+                          max_q_len: int | None = None, max_ctx_len: int | None = None,
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          prefix_splits: int = 0, suffix_splits: int = 0,
+                          workspace: torch.Tensor | None = None, validate: bool = False,
+                          stream=None):
+    """prefill() for sequences that all start with the same prefix_len tokens in
+    the same physical blocks: the prefix is attended once by all query tokens
+    together, each sequence's own keys separately, and the two merged.
+    Returns (o, lse) as prefill() does."""
+    B = int(ctx_lens.numel())
+    T, Hq, D = q.shape
+    if max_q_len is None or max_ctx_len is None or validate:
+        cu = cu_q_lens.cpu()
+        q_lens = (cu[1:] - cu[:-1]).tolist()
+        if max_q_len is None:
+            max_q_len = max(q_lens) if q_lens else 0
+        if max_ctx_len is None:
+            max_ctx_len = int(ctx_lens.max().item()) if B else 0
+        if validate:
+            _validate(pool, ctx_lens, block_table, q_lens)
+            if int(cu[-1]) != T:
+                raise ValueError(f"cu_q_lens ends at {int(cu[-1])}, q has {T} rows")
+            bt = block_table.cpu()
+            n = prefix_len // 16
+            if B and not bool((bt[:, :n] == bt[0:1, :n]).all()):
+                raise ValueError("block tables do not share the prefix pages")
+            cl = ctx_lens.cpu().tolist()
+            for b in range(B):
+                if cl[b] - q_lens[b] < prefix_len:
+                    raise ValueError(f"sequence {b}: a query lies inside the prefix")
+    if B == 0:
+        return (out if out is not None else torch.empty_like(q),
+                lse if lse is not None else torch.empty((T, Hq), dtype=torch.float32,
+                                                        device=q.device))
+    if prefix_splits == 0 or suffix_splits == 0:
+        ap, as_ = shared_prefix_num_splits(B, pool.num_kv_heads, Hq, max_q_len, max_ctx_len,
+                                           prefix_len, T)
+        prefix_splits = prefix_splits or ap
+        suffix_splits = suffix_splits or as_
+    need = shared_prefix_workspace_bytes(T, Hq, D, prefix_splits + suffix_splits)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _check(_prefill_sp(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(cu_q_lens),
+                       _ptr(ctx_lens), _ptr(block_table), block_table.shape[1], B, Hq, max_q_len,
+                       max_ctx_len, scale, 1 if causal else 0, prefix_len, T, prefix_splits,
+                       suffix_splits, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "pa_prefill_shared_prefix")
     return o, lse
 
 

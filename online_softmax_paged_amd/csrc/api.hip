@@ -91,7 +91,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 2; }
+int32_t pa_abi_version(void) { return 3; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
@@ -229,8 +229,84 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
     const size_t o_bytes = (rows * pool->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    a.part_rows = static_cast<int64_t>(num_seqs) * max_q_len;
   }
   return launched(launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_shared_prefix_num_splits(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t num_q_heads, int32_t max_q_len,
+                                      int32_t max_ctx_len, int32_t prefix_len,
+                                      int32_t num_q_tokens, int32_t* prefix_splits,
+                                      int32_t* suffix_splits) {
+  if (!prefix_splits || !suffix_splits || num_seqs < 1 || num_q_tokens < 1 ||
+      prefix_len < 1 || max_ctx_len <= prefix_len)
+    return PA_ERR_INVALID_ARG;
+  // The packed pass is one sequence of all query tokens over the prefix; the
+  // suffix pass is the batch over what follows it (the decode kernel's pass
+  // when every sequence has one query).
+  *prefix_splits = pa_prefill_num_splits(1, num_kv_heads, num_q_heads, num_q_tokens, prefix_len);
+  *suffix_splits =
+      max_q_len == 1
+          ? pa_decode_num_splits(num_seqs, num_kv_heads, max_ctx_len - prefix_len)
+          : pa_prefill_num_splits(num_seqs, num_kv_heads, num_q_heads, max_q_len,
+                                  max_ctx_len - prefix_len);
+  return PA_OK;
+}
+
+size_t pa_shared_prefix_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads,
+                                        int32_t head_dim, int32_t total_splits) {
+  if (num_q_tokens < 1 || num_q_heads < 1 || head_dim < 1 || total_splits < 1) return 0;
+  const size_t rows = static_cast<size_t>(total_splits) * num_q_tokens * num_q_heads;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return o_bytes + rows * sizeof(float);
+}
+
+pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype,
+                                   void* o, float* lse, const int32_t* cu_q_lens,
+                                   const int32_t* ctx_lens, const int32_t* block_table,
+                                   int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_q_len, int32_t max_ctx_len, float scale,
+                                   int32_t causal, int32_t prefix_len, int32_t num_q_tokens,
+                                   int32_t prefix_splits, int32_t suffix_splits,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs == 0 && pool) return check_pool(pool);
+  pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
+                           num_q_heads, max_ctx_len, scale);
+  if (s != PA_OK) return s;
+  if (pool->kv_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (!cu_q_lens || max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
+  if (prefix_len < PA_BLOCK_SIZE || prefix_len % PA_BLOCK_SIZE != 0 ||
+      prefix_len + max_q_len > max_ctx_len)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_tokens < 1 || static_cast<int64_t>(num_q_tokens) >
+                              static_cast<int64_t>(num_seqs) * max_q_len)
+    return PA_ERR_INVALID_ARG;
+  if (prefix_splits < 0 || prefix_splits > 64 || suffix_splits < 0 || suffix_splits > 64)
+    return PA_ERR_INVALID_ARG;
+  int32_t auto_p = 1, auto_s = 1;
+  s = pa_shared_prefix_num_splits(num_seqs, pool->num_kv_heads, num_q_heads, max_q_len,
+                                  max_ctx_len, prefix_len, num_q_tokens, &auto_p, &auto_s);
+  if (s != PA_OK) return s;
+  if (prefix_splits == 0) prefix_splits = auto_p;
+  if (suffix_splits == 0) suffix_splits = auto_s;
+  const int32_t total = prefix_splits + suffix_splits;
+  const size_t need =
+      pa_shared_prefix_workspace_bytes(num_q_tokens, num_q_heads, pool->head_dim, total);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
+                         num_q_heads, max_ctx_len, scale);
+  a.cu_q_lens = cu_q_lens;
+  a.max_q_len = max_q_len;
+  a.causal = causal ? 1 : 0;
+  const size_t rows = static_cast<size_t>(total) * num_q_tokens * num_q_heads;
+  const size_t o_bytes = (rows * pool->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  a.part_rows = num_q_tokens;
+  return launched(launch_prefill_shared_prefix(a, prefix_len, num_q_tokens, prefix_splits,
+                                               suffix_splits, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pa_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len) {

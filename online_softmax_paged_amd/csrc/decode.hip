@@ -117,8 +117,10 @@ void decode_split_kernel(AttnArgs a) {
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
   const int n_pages = (ctx + kPage - 1) / kPage;
   const int max_pages = (a.max_ctx_len + kPage - 1) / kPage;
-  const int pps = (max_pages + S - 1) / S;
-  const int p_begin = split * pps;
+  // pages [key_begin / 16, max_pages) cut into S ranges
+  const int pg0 = a.key_begin / kPage;
+  const int pps = max(0, (max_pages - pg0 + S - 1) / S);
+  const int p_begin = pg0 + split * pps;
   const int p_end = min(p_begin + pps, n_pages);
 
   // Q^T operand: column c = query head g*G + c (zero for c >= G).
@@ -274,9 +276,15 @@ void decode_split_kernel(AttnArgs a) {
     const float out = empty ? 0.f : O / L;
     const float lse = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
     const int64_t row = static_cast<int64_t>(b) * Hq + g * G + hd;
-    if (S == 1) {
+    if (a.ws_o == nullptr) {
       static_cast<uint16_t*>(a.o)[row * D + d] = to_bf16_bits(out);
       if (d == 0 && a.lse) a.lse[row] = lse;
+    } else if (a.part_rows > 0) {
+      // partial rows laid out as the prefill's, sequence b being token b
+      if (b >= a.part_rows) continue;
+      const int64_t prow = static_cast<int64_t>(a.split_base + split) * a.part_rows * Hq + row;
+      a.ws_o[prow * D + d] = out;
+      if (d == 0) a.ws_lse[prow] = lse;
     } else {
       a.ws_o[(row * S + split) * D + d] = out;
       if (d == 0) a.ws_lse[row * S + split] = lse;
@@ -399,6 +407,27 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : M + __logf(W);
 }
 
+// The split pass of a bf16 or fp8 pool (partials, or the output when a has no
+// workspace).
+template <int D>
+hipError_t launch_split_d(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
+  // Stream (non-temporal loads) when the largest possible K/V read of the
+  // call is well beyond the 256 MB last-level cache.
+  const double es = a.kv_dtype == PA_FP8_E4M3 ? 1.0 : 2.0;
+  const double max_bytes = 2.0 * es * D * a.num_kv_heads * static_cast<double>(a.num_seqs) *
+                           (a.max_ctx_len - a.key_begin);
+  const bool nt = max_bytes > 512.0 * (1 << 20);
+  if (a.kv_dtype == PA_FP8_E4M3) {
+    if (nt) decode_split_kernel<D, true, true><<<grid, 256, 0, st>>>(a);
+    else decode_split_kernel<D, true, false><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (nt) decode_split_kernel<D, false, true><<<grid, 256, 0, st>>>(a);
+    else decode_split_kernel<D, false, false><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
   const int S = a.num_splits;
@@ -406,20 +435,7 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
     const dim3 grid(S, (a.num_q_heads + kWaves - 1) / kWaves, a.num_seqs);
     decode_f32_kernel<D><<<grid, 256, 0, st>>>(a);
   } else {
-    const dim3 grid(S, a.num_kv_heads, a.num_seqs);
-    // Stream (non-temporal loads) when the largest possible K/V read of the
-    // call is well beyond the 256 MB last-level cache.
-    const double es = a.kv_dtype == PA_FP8_E4M3 ? 1.0 : 2.0;
-    const double max_bytes =
-        2.0 * es * D * a.num_kv_heads * static_cast<double>(a.num_seqs) * a.max_ctx_len;
-    const bool nt = max_bytes > 512.0 * (1 << 20);
-    if (a.kv_dtype == PA_FP8_E4M3) {
-      if (nt) decode_split_kernel<D, true, true><<<grid, 256, 0, st>>>(a);
-      else decode_split_kernel<D, true, false><<<grid, 256, 0, st>>>(a);
-    } else {
-      if (nt) decode_split_kernel<D, false, true><<<grid, 256, 0, st>>>(a);
-      else decode_split_kernel<D, false, false><<<grid, 256, 0, st>>>(a);
-    }
+    launch_split_d<D>(a, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
@@ -436,6 +452,10 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t st) {
   return a.head_dim == 64 ? launch_decode_d<64>(a, st) : launch_decode_d<128>(a, st);
+}
+
+hipError_t launch_decode_split(const AttnArgs& a, hipStream_t st) {
+  return a.head_dim == 64 ? launch_split_d<64>(a, st) : launch_split_d<128>(a, st);
 }
 
 }  // namespace pa

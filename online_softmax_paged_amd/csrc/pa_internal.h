@@ -120,9 +120,22 @@ struct AttnArgs {
   int32_t max_ctx_len;
   float scale;
   int32_t causal;
-  int32_t num_splits;          // decode only
-  float* ws_o;                 // decode: [B, Hq, S, D] partial outputs
+  int32_t num_splits;          // key splits of this launch (blockIdx.y carries them)
+  float* ws_o;                 // decode: [B, Hq, S, D] partial outputs; prefill: see below
   float* ws_lse;               // decode: [B, Hq, S] partial logsumexp
+  // Prefill partials (ws_o != nullptr): split s of this launch writes the
+  // normalised fp32 row of query token t, head h at
+  // ((split_base + s) * part_rows + t) * Hq + h, t the token's index in q.
+  // A decode launch uses this layout too (token t = sequence t) when
+  // part_rows > 0, else its own [B, Hq, S].
+  int32_t split_base;
+  int64_t part_rows;
+  // Prefill: packed_q > 0 makes the launch one virtual sequence of packed_q
+  // query tokens (all of q) over the first max_ctx_len keys of block-table
+  // row 0; cu_q_lens and ctx_lens are not read.
+  int32_t packed_q;
+  // Keys below this position (a multiple of 16) are left out.
+  int32_t key_begin;
 };
 
 // Full-wave max and sum (64 lanes).
@@ -209,6 +222,10 @@ __device__ __forceinline__ void f32_attend(const AttnArgs& a, const int32_t* bt,
 }
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t st);
+// The decode split pass alone (bf16 or fp8 pool), partials as a's workspace says.
+hipError_t launch_decode_split(const AttnArgs& a, hipStream_t st);
+hipError_t launch_prefill_shared_prefix(const AttnArgs& a, int prefix_len, int num_q_tokens,
+                                        int s_prefix, int s_suffix, hipStream_t st);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t st);
 
 }  // namespace pa

@@ -215,18 +215,17 @@ __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, Smem<D>& sm
   }
 }
 
-// Epilogue of one lane (query row qrow, its half of the features): with one
-// key split, the output row (bf16) and its logsumexp; with several, this
-// split's normalised fp32 partial row and logsumexp in the workspace, at
-// ((split * num_seqs + b) * max_q_len + token) * Hq + head.
+// Epilogue of one lane (query row qrow = token * Hq + head, its half of the
+// features): without a workspace, the output row (bf16) and its logsumexp;
+// with one, this split's normalised fp32 partial row and logsumexp at
+// (split_base + split) * part_rows * Hq + qrow.
 template <int D>
 __device__ __forceinline__ void write_rows(const AttnArgs& a, const f32x16 (&acc)[D / 32],
-                                           float m, float l, int64_t qrow, int b, int tt,
-                                           int h, int split, int half) {
+                                           float m, float l, int64_t qrow, int split, int half) {
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
   const float lse = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
-  if (a.num_splits == 1) {
+  if (a.ws_o == nullptr) {
     uint16_t* op = static_cast<uint16_t*>(a.o) + qrow * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -240,8 +239,9 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const f32x16 (&acc
     if (half == 0 && a.lse) a.lse[qrow] = lse;
     return;
   }
+  if (qrow >= a.part_rows * a.num_q_heads) return;  // token past the partials' rows
   const int64_t prow =
-      ((static_cast<int64_t>(split) * a.num_seqs + b) * a.max_q_len + tt) * a.num_q_heads + h;
+      static_cast<int64_t>(a.split_base + split) * a.part_rows * a.num_q_heads + qrow;
   float* op = a.ws_o + prow * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -267,10 +267,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int split = static_cast<int>(blockIdx.y) % S;
   const int TQ = kRows / G;
 
-  const int q0 = a.cu_q_lens[b];
-  const int qlen = a.cu_q_lens[b + 1] - q0;
-  int ctx = a.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  int q0 = 0, qlen = a.packed_q, ctx = a.max_ctx_len;
+  if (a.packed_q == 0) {
+    q0 = a.cu_q_lens[b];
+    qlen = a.cu_q_lens[b + 1] - q0;
+    ctx = a.ctx_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  }
   const int t0 = tile * TQ;
   if (t0 >= qlen) return;
   const int pos_base = ctx - qlen;            // position of query token 0
@@ -278,9 +281,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   if (kmax <= 0) return;                      // inconsistent lengths: nothing visible
   const int n_kt_all = (kmax + kKeys - 1) / kKeys;
-  // this split's key tiles [kt_begin, n_kt)
-  const int per_split = (n_kt_all + S - 1) / S;
-  const int kt_begin = split * per_split;
+  // this split's key tiles [kt_begin, n_kt), from the tile holding key_begin
+  const int kt_first = a.key_begin / kKeys;
+  const int per_split = max(0, (n_kt_all - kt_first + S - 1) / S);
+  const int kt_begin = kt_first + split * per_split;
   const int n_kt = min(n_kt_all, kt_begin + per_split);
   const int n_pages = (ctx + kPage - 1) / kPage;
   // Tiles whose keys are all visible to every row need no mask.
@@ -349,6 +353,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? sv[i] : -INFINITY;
     }
+    if (kt * kKeys < a.key_begin) {  // key_begin % 32 == 16: the tile's first page is left out
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = -INFINITY;
+    }
     float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sv[i]), sv[i + 1]);
@@ -406,7 +414,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 
   l = sum_xor32(l);
   if (!row_ok) return;
-  write_rows<D>(a, acc, m, l, qrow, b, tt, g * G + hg, split, half);
+  write_rows<D>(a, acc, m, l, qrow, split, half);
 }
 
 // ---------------------------------------------------------------------------
@@ -613,10 +621,13 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
       wait_vmcnt_upto4(plan.count);
   };
 
-  const int q0 = a.cu_q_lens[b];
-  const int qlen = a.cu_q_lens[b + 1] - q0;
-  int ctx = a.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  int q0 = 0, qlen = a.packed_q, ctx = a.max_ctx_len;
+  if (a.packed_q == 0) {
+    q0 = a.cu_q_lens[b];
+    qlen = a.cu_q_lens[b + 1] - q0;
+    ctx = a.ctx_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  }
   const int t0 = tile * TQ;
   if (t0 >= qlen) return;
   const int pos_base = ctx - qlen;
@@ -624,9 +635,10 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   if (kmax <= 0) return;
   const int n_kt_all = (kmax + kKeys - 1) / kKeys;
-  // this split's key tiles [kt_begin, n_kt)
-  const int per_split = (n_kt_all + S - 1) / S;
-  const int kt_begin = split * per_split;
+  // this split's key tiles [kt_begin, n_kt), from the tile holding key_begin
+  const int kt_first = a.key_begin / kKeys;
+  const int per_split = max(0, (n_kt_all - kt_first + S - 1) / S);
+  const int kt_begin = kt_first + split * per_split;
   const int n_kt = min(n_kt_all, kt_begin + per_split);
   const int n_pages = (ctx + kPage - 1) / kPage;
   const int first_pos = pos_base + t0;
@@ -730,6 +742,10 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? sv[i] : -INFINITY;
     }
+    if (kt * kKeys < a.key_begin) {  // key_begin % 32 == 16: the tile's first page is left out
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = -INFINITY;
+    }
     float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sv[i]), sv[i + 1]);
@@ -782,7 +798,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   wait_vmcnt<0>();  // no DMA of this workgroup outlives it
   l = sum_xor32(l);
   if (!row_ok) return;
-  write_rows<D>(a, acc, m, l, qrow, b, tt, g * G + hg, split, half);
+  write_rows<D>(a, acc, m, l, qrow, split, half);
 }
 
 // fp32 pools: one wave per (query row, query head), 64 keys per step (see
@@ -830,33 +846,89 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int Hq = a.num_q_heads, S = a.num_splits;
   const int64_t per_seq = static_cast<int64_t>(a.max_q_len) * Hq;
-  const int64_t stride = per_seq * a.num_seqs;  // partial rows per split
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (r >= stride) return;
+  if (r >= per_seq * a.num_seqs) return;
   const int b = static_cast<int>(r / per_seq);
   const int i = static_cast<int>((r % per_seq) / Hq), h = static_cast<int>(r % Hq);
   const int q0 = a.cu_q_lens[b];
   if (i >= a.cu_q_lens[b + 1] - q0) return;
+  const int64_t row = static_cast<int64_t>(q0 + i) * Hq + h;  // token row, as in the partials
+  const int64_t stride = a.part_rows * Hq;                     // partial rows per split
+  if (row >= stride) return;
+  // lane s holds split s's logsumexp and weight (64 splits at a time)
   float M = -INFINITY;
-  for (int t = 0; t < S; ++t) M = fmaxf(M, a.ws_lse[t * stride + r]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, a.ws_lse[s * stride + row]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   const float Mu = M == -INFINITY ? 0.f : M;
   constexpr int NPL = D / 64;
   float acc[NPL] = {};
   float W = 0.f;
-  for (int t = 0; t < S; ++t) {
-    const float lt = a.ws_lse[t * stride + r];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    const float lt = s < S ? a.ws_lse[s * stride + row] : -INFINITY;
     const float w = lt == -INFINITY ? 0.f : fast_exp2((lt - Mu) * kLog2e);
     W += w;
-    const float* op = a.ws_o + (t * stride + r) * D + lane;
+    const int n = min(64, S - s0);
+    const float* op = a.ws_o + (s0 * stride + row) * D + lane;
+    const int wbits = __builtin_bit_cast(int, w);
+    int k = 0;
+    for (; k + 8 <= n; k += 8) {  // 8 splits' loads in flight at once
+      float x[8][NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) acc[j] += w * op[64 * j];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) x[u][j] = op[(k + u) * stride * D + 64 * j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, k + u));
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) acc[j] += wk * x[u][j];
+      }
+    }
+    for (; k < n; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, k));
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[j] += wk * op[k * stride * D + 64 * j];
+    }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
   const bool empty = !(W > 0.f);
-  const int64_t row = static_cast<int64_t>(q0 + i) * Hq + h;
+  const float inv = empty ? 0.f : 1.f / W;
 #pragma unroll
   for (int j = 0; j < NPL; ++j)
-    static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] = to_bf16_bits(empty ? 0.f : acc[j] / W);
+    static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] = to_bf16_bits(acc[j] * inv);
   if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : M + __logf(W);
+}
+
+// One pass of the bf16 or fp8 kernel over a's sequences (or its packed
+// queries) and key range, num_splits splits.
+template <int D>
+hipError_t launch_pass(const AttnArgs& a, hipStream_t st) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+  constexpr int NW = PA_PREFILL_WAVES;
+  const int TQ = (a.kv_dtype == PA_BF16 ? 32 * NW : kRows) / G;
+  const int n_q = a.packed_q > 0 ? a.packed_q : a.max_q_len;
+  const int n_tiles = (n_q + TQ - 1) / TQ;
+  const int n_seq = a.packed_q > 0 ? 1 : a.num_seqs;
+  const dim3 grid(n_seq * a.num_kv_heads, n_tiles * a.num_splits);
+  if (a.kv_dtype == PA_FP8_E4M3)
+    prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
+  else
+    prefill_dma_kernel<D, NW><<<grid, 64 * NW, 0, st>>>(a, n_tiles);
+  return hipGetLastError();
+}
+
+// Merge of the S = a.num_splits partials of every query row into o and lse.
+template <int D>
+hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.max_q_len * a.num_q_heads;
+  prefill_merge_kernel<D><<<static_cast<unsigned>((rows + 3) / 4), 256, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -866,29 +938,53 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
     prefill_f32_kernel<D><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
-  const int G = a.num_q_heads / a.num_kv_heads;
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 4
-#endif
-  constexpr int NW = PA_PREFILL_WAVES;
-  const int TQ = (a.kv_dtype == PA_BF16 ? 32 * NW : kRows) / G;
-  const int n_tiles = (a.max_q_len + TQ - 1) / TQ;
-  const dim3 grid(a.num_seqs * a.num_kv_heads, n_tiles * a.num_splits);
-  if (a.kv_dtype == PA_FP8_E4M3)
-    prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
-  else
-    prefill_dma_kernel<D, NW><<<grid, 64 * NW, 0, st>>>(a, n_tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_splits == 1) return e;
-  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.max_q_len * a.num_q_heads;
-  prefill_merge_kernel<D><<<static_cast<unsigned>((rows + 3) / 4), 256, 0, st>>>(a);
-  return hipGetLastError();
+  hipError_t e = launch_pass<D>(a, st);
+  if (e != hipSuccess || a.ws_o == nullptr) return e;
+  return launch_merge<D>(a, st);
+}
+
+// Shared prefix: the first prefix_len keys (whole pages, the same physical
+// blocks for every sequence) are attended once by all query tokens packed
+// into one virtual sequence (no mask: every query lies past the prefix),
+// into partials 0..s_prefix-1; each sequence's own keys from prefix_len on
+// go to partials s_prefix..s_prefix+s_suffix-1; the merge combines them.
+template <int D>
+hipError_t launch_shared_prefix_d(const AttnArgs& a, int prefix_len, int num_q_tokens,
+                                  int s_prefix, int s_suffix, hipStream_t st) {
+  AttnArgs p = a;
+  p.packed_q = num_q_tokens;
+  p.max_ctx_len = prefix_len;
+  p.causal = 0;
+  p.key_begin = 0;
+  p.split_base = 0;
+  p.num_splits = s_prefix;
+  hipError_t e = launch_pass<D>(p, st);
+  if (e != hipSuccess) return e;
+  AttnArgs q = a;
+  q.packed_q = 0;
+  q.key_begin = prefix_len;
+  q.split_base = s_prefix;
+  q.num_splits = s_suffix;
+  // one query per sequence: the suffixes go through the decode kernel, which
+  // streams pages for a single row instead of multiplying a 128-row tile
+  e = a.max_q_len == 1 ? launch_decode_split(q, st) : launch_pass<D>(q, st);
+  if (e != hipSuccess) return e;
+  AttnArgs m = a;
+  m.num_splits = s_prefix + s_suffix;
+  return launch_merge<D>(m, st);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t st) {
   return a.head_dim == 64 ? launch_prefill_d<64>(a, st) : launch_prefill_d<128>(a, st);
+}
+
+hipError_t launch_prefill_shared_prefix(const AttnArgs& a, int prefix_len, int num_q_tokens,
+                                        int s_prefix, int s_suffix, hipStream_t st) {
+  return a.head_dim == 64
+             ? launch_shared_prefix_d<64>(a, prefix_len, num_q_tokens, s_prefix, s_suffix, st)
+             : launch_shared_prefix_d<128>(a, prefix_len, num_q_tokens, s_prefix, s_suffix, st);
 }
 
 }  // namespace pa

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 2
+    assert pa.abi_version() == 3
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -161,6 +161,40 @@ def test_prefill_split_checks_and_heuristic():
     assert pa.prefill_num_splits(8, 8, 32, 256, 1536) == 1
     assert pa.prefill_num_splits(1, 8, 32, 256, 8192) == 8
     assert pa.prefill_num_splits(1, 1, 1, 10, 100) == 1
+
+
+def _shared(pool, **kw):
+    a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, cu=0x8000, ctx=0x9000,
+             bt=0xa000, stride=8, B=2, Hq=8, max_q=32, max_ctx=128, scale=0.1, causal=1,
+             prefix=64, T=40, sp=1, ss=1, ws=0, ws_bytes=0)
+    a.update(kw)
+    return pa._prefill_sp(pool.c, a["q"], a["q_dtype"], a["o"], a["lse"], a["cu"], a["ctx"],
+                          a["bt"], a["stride"], a["B"], a["Hq"], a["max_q"], a["max_ctx"],
+                          a["scale"], a["causal"], a["prefix"], a["T"], a["sp"], a["ss"],
+                          a["ws"], a["ws_bytes"], None)
+
+
+def test_shared_prefix_checks():
+    need = pa.shared_prefix_workspace_bytes(40, 8, 128, 2)
+    assert need >= 2 * 40 * 8 * (128 + 1) * 4
+    assert pa.shared_prefix_workspace_bytes(0, 8, 128, 2) == 0
+    p = _FakePool()
+    assert _shared(_FakePool(kv_dtype=pa.PA_F32), q_dtype=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
+    assert _shared(p) == pa.PA_ERR_WORKSPACE                       # always needs a workspace
+    assert _shared(p, ws=0x10000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
+    assert _shared(p, ws=0x10008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG   # misaligned
+    for bad in (dict(prefix=0), dict(prefix=24), dict(prefix=112),  # not whole pages; no room
+                dict(T=0), dict(T=65), dict(sp=65), dict(ss=-1), dict(cu=0),
+                dict(max_q=0)):
+        assert _shared(p, **bad) == pa.PA_ERR_INVALID_ARG, bad
+    assert _shared(p, B=0) == pa.PA_OK
+    # split choice: the packed prefix pass has few query tiles, so its keys split
+    sp, ss = pa.shared_prefix_num_splits(8, 8, 32, 1, 32768, 32768 - 64, 8)
+    assert sp > 1 and ss == 1
+    sp, ss = pa.shared_prefix_num_splits(16, 8, 32, 256, 1536, 1024, 2056)
+    assert sp == 1 and ss == 1
+    with pytest.raises(pa.PAError):
+        pa.shared_prefix_num_splits(1, 8, 32, 1, 64, 64, 1)
 
 
 def test_decode_split_heuristic():

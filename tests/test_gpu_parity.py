@@ -250,6 +250,90 @@ def test_mixed_batch_in_one_prefill_call():
     assert (lse[rows] - ld).abs().max() <= 1e-3
 
 
+# ------------------------------------------------------------ shared prefix
+def _run_shared(wl, call, pool, prefix, **kw):
+    dc = H.DeviceCall(wl, call)
+    return pa.prefill_shared_prefix(pool, dc.q, dc.cu_q_lens, dc.ctx_lens, dc.block_table,
+                                    wl.scale, prefix, causal=call.causal,
+                                    max_q_len=dc.max_q_len, max_ctx_len=dc.max_ctx_len,
+                                    validate=True, **kw)
+
+
+SHARED_CASES = [
+    # kv, D, Hq, Hkv, prefix, ctx_lens, q_lens, causal
+    ("bf16", 128, 8, 2, 64, (200, 130, 300, 65), (64, 1, 100, 1), True),
+    ("bf16", 128, 8, 2, 48, (200, 130, 300, 49), (64, 1, 100, 1), True),   # prefix ends mid-tile
+    ("bf16", 64, 16, 2, 96, (400, 97, 250), (1, 1, 150), False),
+    ("fp8", 128, 8, 2, 64, (200, 130, 300, 65), (64, 1, 100, 1), True),
+    ("fp8", 128, 8, 1, 48, (90, 333, 61), (17, 200, 1), True),
+    ("fp8", 64, 4, 4, 128, (129, 140, 700, 300), (1, 12, 1, 172), False),
+]
+
+
+@pytest.mark.parametrize("kv,D,Hq,Hkv,prefix,ctx,ql,causal", SHARED_CASES)
+@pytest.mark.parametrize("splits", [(0, 0), (1, 1), (3, 2)])
+def test_shared_prefix_parity(kv, D, Hq, Hkv, prefix, ctx, ql, causal, splits):
+    """Queries of sequences that share their first pages: prefix attended once
+    by all queries packed together, suffixes per sequence, merged; the result
+    matches the oracle (which knows nothing of the sharing) and pa_prefill."""
+    _log(f"shared prefix kv={kv} D={D} Hq={Hq} Hkv={Hkv} prefix={prefix} ctx={ctx} "
+         f"q={ql} causal={causal} splits={splits}")
+    wl = workloads.small("prefill", kv_dtype=kv, q_dtype="bf16", num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=D, ctx_lens=ctx, q_lens=ql, seed=90 + D,
+                         shared_prefix=prefix, causal=causal)
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    call = wl.calls[0]
+    o, lse = _run_shared(wl, call, pool, prefix, prefix_splits=splits[0],
+                         suffix_splits=splits[1])
+    torch.cuda.synchronize()
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    tol = H.tolerance(wl)
+    _log(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e} tol={tol}")
+    assert eo <= tol and el <= tol
+    o2, l2 = H.DeviceCall(wl, call).run(pool, num_splits=1)
+    assert (o.float() - o2.float()).abs().max().item() <= tol
+    assert (lse - l2).abs().max().item() <= 1e-3
+
+
+def test_shared_prefix_mixed_step_full_size():
+    """The 16-sequence fp8 mixed step (8 chunks of 256 and 8 decode rows over a
+    shared 1024-token prefix) as one shared-prefix call, in the benchmark's
+    configuration, against the oracle on every row."""
+    _log("shared prefix: mixed fp8 16x1536 as one call")
+    wl, opool = _named(5)
+    pool = H.device_pool(wl)
+    call = workloads.one_call(wl)
+    o, lse = _run_shared(wl, call, pool, wl.shared_prefix)
+    torch.cuda.synchronize()
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    _log(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= H.TOL["fp8"] and el <= H.TOL["fp8"]
+    # repeat: bitwise the same
+    o2, l2 = _run_shared(wl, call, pool, wl.shared_prefix)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_shared_prefix_decode_only_splits_the_prefix():
+    """Decode rows only (one token per sequence) over a long shared prefix: the
+    packed prefix pass has one query tile per KV head, so its keys are split."""
+    _log("shared prefix: decode rows over a 4096-token prefix")
+    wl = workloads.small("prefill", kv_dtype="bf16", q_dtype="bf16", num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, ctx_lens=(4200, 4097, 4400, 4111),
+                         q_lens=(1, 1, 1, 1), seed=97, shared_prefix=4096)
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    call = wl.calls[0]
+    sp, ss = pa.shared_prefix_num_splits(4, 8, 32, 1, 4400, 4096, 4)
+    assert sp > 1
+    o, lse = _run_shared(wl, call, pool, 4096)
+    torch.cuda.synchronize()
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    _log(f"  splits={sp},{ss} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= H.TOL["bf16"] and el <= H.TOL["bf16"]
+
+
 @pytest.mark.parametrize("k", [1, 2, 4, 5])
 def test_named_workload_full(k):
     _log(f"named workload {k}")

@@ -160,6 +160,26 @@ def build(name: str, *, kv_dtype: str, q_dtype: str, num_q_heads: int,
         seed=seed, shared_prefix=shared_prefix)
 
 
+def one_call(wl: Workload) -> Call:
+    """The workload's calls joined into one varlen call: sequences and query
+    tokens in call order (a decode query is a one-token chunk at the last
+    position).  Only concatenation; nothing is drawn."""
+    seqs, q_lens = [], []
+    for c in wl.calls:
+        seqs += c.seqs
+        q_lens += c.q_lens
+    assert len(set(c.causal for c in wl.calls)) == 1
+    out = Call("prefill", seqs, q_lens, wl.calls[0].causal)
+    out.q = torch.cat([c.q for c in wl.calls])
+    out.ctx_lens = torch.tensor([wl.ctx_lens[s] for s in seqs], dtype=torch.int32)
+    cu = [0]
+    for x in q_lens:
+        cu.append(cu[-1] + x)
+    out.cu_q_lens = torch.tensor(cu, dtype=torch.int32)
+    out.block_table = wl.block_tables[torch.tensor(seqs, dtype=torch.long)].contiguous()
+    return out
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.  Seeds are 1000 + k for workload k.
 
@@ -224,7 +244,8 @@ NAMED = {
 
 def small(kind: str, *, kv_dtype="bf16", q_dtype="bf16", num_q_heads=8,
           num_kv_heads=2, head_dim=128, ctx_lens=(100, 37, 300), q_lens=None,
-          seed=7, shared_prefix=0, spare_pages=8, src_dtype=None) -> Workload:
+          seed=7, shared_prefix=0, spare_pages=8, src_dtype=None,
+          causal=True) -> Workload:
     """A small workload of the same structure, for parity at oracle-friendly size."""
     ctx_lens = list(ctx_lens)
     B = len(ctx_lens)
@@ -232,7 +253,7 @@ def small(kind: str, *, kv_dtype="bf16", q_dtype="bf16", num_q_heads=8,
         calls = [Call("decode", list(range(B)), [1] * B)]
     elif kind == "prefill":
         q_lens = list(q_lens) if q_lens is not None else list(ctx_lens)
-        calls = [Call("prefill", list(range(B)), q_lens)]
+        calls = [Call("prefill", list(range(B)), q_lens, causal)]
     else:
         raise ValueError(kind)
     return build(f"small_{kind}_{kv_dtype}", kv_dtype=kv_dtype, q_dtype=q_dtype,
