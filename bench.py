@@ -295,7 +295,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--decode-splits", type=int, default=0,
-                    help="KV splits for decode calls (0 = the library's choice)")
+                    help="KV splits for decode calls (0 = the library's choice, "
+                         "-1 = balanced chunks across sequences)")
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="MB of scratch written between steps to evict the 256 MB last-level "
                          "cache (-1 = 512 when a decode call reads less than 512 MB of KV)")
@@ -360,8 +361,11 @@ def main():
                                  max_ctx_len=mc, out=o, lse=lse, num_splits=S, workspace=ws))
             else:
                 B, Hq, D = q.shape
-                S = args.decode_splits or pa.decode_num_splits(B, wl.num_kv_heads, mc)
-                ws = torch.empty(max(1, pa.decode_workspace_bytes(B, Hq, D, S)), dtype=torch.uint8, device=dev)
+                S = args.decode_splits or pa.decode_choose_splits(
+                    B, wl.num_kv_heads, mc, int(call.ctx_lens.sum()))
+                nws = (pa.decode_balanced_workspace_bytes(B, Hq, wl.num_kv_heads, D, mc)
+                       if S == pa.DECODE_BALANCED else pa.decode_workspace_bytes(B, Hq, D, S))
+                ws = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
                 fn = (lambda pool=pool, q=q, ctx=ctx, bt=bt, mc=mc, o=o, lse=lse, wl=wl, ws=ws, S=S:
                       pa.decode(pool, q, ctx, bt, wl.scale, max_ctx_len=mc, num_splits=S,
                                 workspace=ws, out=o, lse=lse))

@@ -263,12 +263,28 @@ pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dty
  *   o   : same shape and dtype (device, written)
  *   lse : float [num_seqs, num_q_heads] (device, written; may be NULL)
  * num_splits: 0 = choose with pa_decode_num_splits(); 1 = no merge pass, no
- *   workspace needed.  workspace: device memory of at least
+ *   workspace needed; at most 256.  workspace: device memory of at least
  *   pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, splits) bytes,
  *   16-byte aligned, contents need not be initialised.  Same dtype and group
  *   support as pa_prefill.
+ * num_splits = PA_DECODE_BALANCED (bf16 and fp8 pools): the pages of all
+ *   sequences of a KV head, taken in sequence order, are cut into equal
+ *   chunks, one per wave, whatever the mix of lengths; a sequence inside one
+ *   chunk is finished there, the others are merged from one partial per chunk
+ *   they meet (same merge as above).  For batches whose longest sequence is
+ *   far above the mean.  workspace: pa_decode_balanced_workspace_bytes(...)
+ *   bytes, 16-byte aligned, contents need not be initialised.
+ * pa_decode_choose_splits: the library's choice given the batch's total
+ *   context length (sum of ctx_len_b; 0 = unknown): PA_DECODE_BALANCED when
+ *   the longest sequence is over 3 times the mean, else pa_decode_num_splits.
  */
+#define PA_DECODE_BALANCED (-1)
+size_t pa_decode_balanced_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_ctx_len);
 int32_t pa_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len);
+int32_t pa_decode_choose_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len,
+                                int64_t total_ctx_len);
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t num_splits);
 pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,

@@ -63,7 +63,9 @@ _prefill_sp = _sig("pa_prefill_shared_prefix", ctypes.c_int,
                    [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                     _F, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP])
 _num_splits = _sig("pa_decode_num_splits", _I32, [_I32, _I32, _I32])
+_choose_splits = _sig("pa_decode_choose_splits", _I32, [_I32, _I32, _I32, ctypes.c_int64])
 _dec_ws = _sig("pa_decode_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
+_dec_bal_ws = _sig("pa_decode_balanced_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32, _I32])
 _decode = _sig("pa_decode", ctypes.c_int,
                [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F, _I32,
                 _VP, _SZ, _VP])
@@ -85,7 +87,10 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks",
             "pa_append_kv", "pa_copy_blocks", "pa_plan_append", "pa_prefill_num_splits",
             "pa_prefill_workspace_bytes", "pa_shared_prefix_num_splits",
-            "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix"]
+            "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
+            "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits"]
+
+DECODE_BALANCED = -1
 
 
 class PAError(RuntimeError):
@@ -349,23 +354,48 @@ def decode_num_splits(num_seqs: int, num_kv_heads: int, max_ctx_len: int) -> int
     return int(_num_splits(num_seqs, num_kv_heads, max_ctx_len))
 
 
+def decode_choose_splits(num_seqs: int, num_kv_heads: int, max_ctx_len: int,
+                         total_ctx_len: int) -> int:
+    """Split count, or DECODE_BALANCED for batches of very uneven lengths."""
+    return int(_choose_splits(num_seqs, num_kv_heads, max_ctx_len, total_ctx_len))
+
+
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
     return int(_dec_ws(num_seqs, num_q_heads, head_dim, num_splits))
+
+
+def decode_balanced_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, max_ctx_len: int) -> int:
+    return int(_dec_bal_ws(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx_len))
 
 
 def decode(pool: KVPool, q: torch.Tensor, ctx_lens, block_table, scale: float,
            max_ctx_len: int | None = None, num_splits: int = 0,
            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-           lse: torch.Tensor | None = None, validate: bool = False, stream=None):
-    """One query per sequence at its last position.  Returns (o, lse)."""
+           lse: torch.Tensor | None = None, validate: bool = False, stream=None,
+           total_ctx_len: int | None = None):
+    """One query per sequence at its last position.  Returns (o, lse).
+    With num_splits = 0 the library chooses; total_ctx_len (the sum of the
+    lengths, if the caller knows it) lets it pick the balanced kernel for very
+    uneven batches.  Lengths are read back from the device only when
+    max_ctx_len is not given."""
     B, Hq, D = q.shape
     if max_ctx_len is None:
-        max_ctx_len = int(ctx_lens.max().item())
+        cl = ctx_lens.cpu()
+        max_ctx_len = int(cl.max().item())
+        if total_ctx_len is None:
+            total_ctx_len = int(cl.clamp(min=0).sum().item())
     if validate:
         _validate(pool, ctx_lens, block_table)
     if num_splits == 0:
-        num_splits = decode_num_splits(B, pool.num_kv_heads, max_ctx_len)
-    need = decode_workspace_bytes(B, Hq, D, num_splits)
+        if pool.kv_dtype != "f32" and total_ctx_len:
+            num_splits = decode_choose_splits(B, pool.num_kv_heads, max_ctx_len, total_ctx_len)
+        else:
+            num_splits = decode_num_splits(B, pool.num_kv_heads, max_ctx_len)
+    if num_splits == DECODE_BALANCED:
+        need = decode_balanced_workspace_bytes(B, Hq, pool.num_kv_heads, D, max_ctx_len)
+    else:
+        need = decode_workspace_bytes(B, Hq, D, num_splits)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = out if out is not None else torch.empty_like(q)

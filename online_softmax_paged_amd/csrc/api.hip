@@ -91,7 +91,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 3; }
+int32_t pa_abi_version(void) { return 4; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
@@ -311,17 +311,38 @@ pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dty
 
 int32_t pa_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len) {
   if (num_seqs < 1 || num_kv_heads < 1 || max_ctx_len < 1) return 1;
-  const int32_t pages = (max_ctx_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
-  // Aim for about 512 workgroups (two per compute unit, all resident at once)
-  // while keeping at least 8 pages (2 per wave) in every split.  Measured on
-  // 8 x 32768 tokens: 8 splits 179 us, 16 splits 187 us, 32 splits 205 us.
+  // With one workgroup per compute unit or more, splitting only adds partial
+  // traffic and a merge (32 x 128..2048 tokens: 36.4 us unsplit, 42.5 us
+  // with 2 splits; 32 x 2048: 50.6 / 56.0 us; 256 x 256: 62.4 / 82.6 us).
+  // Below that, aim for about 512 workgroups (two per compute unit, all
+  // resident) while keeping at least 8 pages (2 per wave) in every split
+  // (8 x 32768 tokens: 8 splits 171 us, 16 splits 187 us, 32 splits 205 us).
   const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  if (base >= 256) return 1;
+  const int32_t pages = (max_ctx_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
   int64_t s = (512 + base - 1) / base;
   int64_t max_by_pages = pages / 8;
   if (s > max_by_pages) s = max_by_pages;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return static_cast<int32_t>(s);
+}
+
+int32_t pa_decode_choose_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len,
+                                int64_t total_ctx_len) {
+  if (num_seqs < 1 || num_kv_heads < 1 || max_ctx_len < 1) return 1;
+  // A batch whose longest sequence is well above the mean leaves most
+  // compute units idle in the split kernel (one workgroup per sequence and
+  // split); the balanced kernel gives every wave the same number of pages.
+  // 1 x 32768 + 31 x 256 tokens: 251.5 us with the split heuristic, 78.9 us
+  // with the best split count, 52.5 us balanced; 4 x 8192 + 60 x 128: 128.4,
+  // 61.0 and 44.5 us.  For even lengths the split kernel is faster (32 x
+  // 1088: 30.6 us against 40.6 us; 32 x 128..2048, max/mean 1.9: 36.4 us
+  // against 40.0 us).
+  if (num_seqs >= 2 && total_ctx_len > 0 &&
+      static_cast<double>(max_ctx_len) * num_seqs > 3.0 * static_cast<double>(total_ctx_len))
+    return PA_DECODE_BALANCED;
+  return pa_decode_num_splits(num_seqs, num_kv_heads, max_ctx_len);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -333,6 +354,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return o_bytes + rows * sizeof(float);
 }
 
+size_t pa_decode_balanced_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_ctx_len) {
+  if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_ctx_len < 1)
+    return 0;
+  return balanced_ws_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx_len, 0);
+}
+
 pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
                     float* lse, const int32_t* ctx_lens, const int32_t* block_table,
                     int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
@@ -342,11 +371,25 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, voi
   pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
                            num_q_heads, max_ctx_len, scale);
   if (s != PA_OK) return s;
-  if (num_splits < 0 || num_splits > 256) return PA_ERR_INVALID_ARG;
+  if (num_splits < PA_DECODE_BALANCED || num_splits > 256) return PA_ERR_INVALID_ARG;
   if (num_splits == 0) num_splits = pa_decode_num_splits(num_seqs, pool->num_kv_heads, max_ctx_len);
   AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
                          num_q_heads, max_ctx_len, scale);
   a.num_splits = num_splits;
+  if (num_splits == PA_DECODE_BALANCED) {
+    if (pool->kv_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+    const size_t need = balanced_ws_bytes(num_seqs, num_q_heads, pool->num_kv_heads,
+                                          pool->head_dim, max_ctx_len, 0);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+    const int64_t U = 4 * static_cast<int64_t>(
+                              balanced_wgs(num_seqs, pool->num_kv_heads, max_ctx_len, 0));
+    const size_t prow = static_cast<size_t>(num_q_heads) * (U + num_seqs);
+    const size_t o_bytes = (prow * pool->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    return launched(launch_decode(a, static_cast<hipStream_t>(stream)));
+  }
   if (num_splits > 1) {
     size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim, num_splits);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;

@@ -100,6 +100,91 @@ __device__ __forceinline__ bool valid_block(int32_t phys, int32_t nb) {
   return phys >= 0 && phys < nb;
 }
 
+// Q^T operand of the score MFMA for sequence b's query heads g*G .. g*G+G-1:
+// lane column c = head g*G + c (zero for c >= G), lane group grp = features
+// ks*32 + grp*8 .. +7.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const AttnArgs& a, int b, int g,
+                                       int G, int c, int grp) {
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                       (static_cast<int64_t>(b) * a.num_q_heads + g * G + (c < G ? c : 0)) * D;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + grp * 8);
+    if (c >= G) v = bf16x8{};
+    qf[ks] = v;
+  }
+}
+
+// One wave's online-softmax state over some pages of one (sequence, KV head),
+// for the G query heads: lane column c = lane % 16 is head c; lane group grp =
+// lane / 16 holds keys grp*4 .. grp*4+3 of every page and features
+// db*16 + grp*4 + i of the accumulator.  m (log2 domain) is the same in the
+// four groups; l is the group's share of the running sum.
+template <int D>
+struct DecodeState {
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[D / 16];
+  __device__ __forceinline__ DecodeState() {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Fold page p of the sequence (keys 16p .. 16p+15; keys >= ctx masked), loaded
+// in f, into the state.  sc = scale * log2(e).
+template <int D, bool FP8>
+__device__ __forceinline__ void fold_page(DecodeState<D>& st, KVFrag<D>& f,
+                                          const bf16x8 (&qf)[D / 32], int p, int ctx, float sc,
+                                          int grp) {
+  f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[ks], qf[ks], s4, 0, 0, 0);
+  float scl = sc, vscl = 1.f;
+  if constexpr (FP8) {
+    scl *= f.ks;
+    vscl = f.vs;
+  }
+  const int key0 = p * kPage + grp * 4;
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = (key0 + i < ctx) ? s4[i] * scl : -INFINITY;
+  float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  mt = max_xor16(mt);
+  mt = max_xor32(mt);
+  const float m_new = fmaxf(st.m, mt);
+  const float alpha = fast_exp2(st.m - m_new);
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
+  st.l = st.l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  st.m = m_new;
+  u32x2 pp;
+  pp.x = pack_bf16x2(pr[0] * vscl, pr[1] * vscl);
+  pp.y = pack_bf16x2(pr[2] * vscl, pr[3] * vscl);
+  const bf16x4 pf = __builtin_bit_cast(bf16x4, pp);
+  if (p * kPage + kPage > ctx) {
+    // Last, partly filled page: slots past the context hold unspecified
+    // bytes (possibly NaN); replace them so that 0 * NaN cannot occur.
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      u32x2 w = __builtin_bit_cast(u32x2, f.v[db]);
+      if (key0 + 0 >= ctx) w.x &= 0xffff0000u;
+      if (key0 + 1 >= ctx) w.x &= 0x0000ffffu;
+      if (key0 + 2 >= ctx) w.y &= 0xffff0000u;
+      if (key0 + 3 >= ctx) w.y &= 0x0000ffffu;
+      f.v[db] = __builtin_bit_cast(bf16x4, w);
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    st.acc[db] *= alpha;
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(i16x4, f.v[db]), __builtin_bit_cast(i16x4, pf), st.acc[db], 0, 0, 0);
+  }
+}
+
 #ifndef PA_DECODE_WAVES_PER_EU
 #define PA_DECODE_WAVES_PER_EU 2
 #endif
@@ -123,75 +208,14 @@ void decode_split_kernel(AttnArgs a) {
   const int p_begin = pg0 + split * pps;
   const int p_end = min(p_begin + pps, n_pages);
 
-  // Q^T operand: column c = query head g*G + c (zero for c >= G).
   bf16x8 qf[D / 32];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<int64_t>(b) * Hq + g * G + (c < G ? c : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + grp * 8);
-      if (c >= G) v = bf16x8{};
-      qf[ks] = v;
-    }
-  }
+  load_q<D>(qf, a, b, g, G, c, grp);
   const float sc = a.scale * kLog2e;
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Fold one page (loaded in f) into the running state.
+  DecodeState<D> st;
   auto process = [&](KVFrag<D>& f, int p, bool valid) {
-    if (!valid) return;
-    f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[ks], qf[ks], s4, 0, 0, 0);
-    float scl = sc, vscl = 1.f;
-    if constexpr (FP8) {
-      scl *= f.ks;
-      vscl = f.vs;
-    }
-    const int key0 = p * kPage + grp * 4;
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = (key0 + i < ctx) ? s4[i] * scl : -INFINITY;
-    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mt = max_xor16(mt);
-    mt = max_xor32(mt);
-    const float m_new = fmaxf(m, mt);
-    const float alpha = fast_exp2(m - m_new);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
-    l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    m = m_new;
-    u32x2 pp;
-    pp.x = pack_bf16x2(pr[0] * vscl, pr[1] * vscl);
-    pp.y = pack_bf16x2(pr[2] * vscl, pr[3] * vscl);
-    const bf16x4 pf = __builtin_bit_cast(bf16x4, pp);
-    if (p * kPage + kPage > ctx) {
-      // Last, partly filled page: slots past the context hold unspecified
-      // bytes (possibly NaN); replace them so that 0 * NaN cannot occur.
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        u32x2 w = __builtin_bit_cast(u32x2, f.v[db]);
-        if (key0 + 0 >= ctx) w.x &= 0xffff0000u;
-        if (key0 + 1 >= ctx) w.x &= 0x0000ffffu;
-        if (key0 + 2 >= ctx) w.y &= 0xffff0000u;
-        if (key0 + 3 >= ctx) w.y &= 0x0000ffffu;
-        f.v[db] = __builtin_bit_cast(bf16x4, w);
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      acc[db] *= alpha;
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(i16x4, f.v[db]), __builtin_bit_cast(i16x4, pf), acc[db], 0, 0, 0);
-    }
+    if (valid) fold_page<D, FP8>(st, f, qf, p, ctx, sc, grp);
   };
 
   // This wave's pages are p_begin + wave + 4*i.  Their block ids are read up
@@ -240,19 +264,18 @@ void decode_split_kernel(AttnArgs a) {
   }
 
   // Row sums: each lane group holds a quarter of the keys of head c.
-  l = sum_xor16(l);
-  l = sum_xor32(l);
+  const float l = sum_xor32(sum_xor16(st.l));
 
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
   __shared__ float sm_o[kWaves][D][17];
   if (grp == 0) {
-    sm_m[wave][c] = m;
+    sm_m[wave][c] = st.m;
     sm_l[wave][c] = l;
   }
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[wave][db * 16 + grp * 4 + i][c] = acc[db][i];
+    for (int i = 0; i < 4; ++i) sm_o[wave][db * 16 + grp * 4 + i][c] = st.acc[db][i];
   __syncthreads();
 
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
@@ -290,6 +313,220 @@ void decode_split_kernel(AttnArgs a) {
       if (d == 0) a.ws_lse[row * S + split] = lse;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced decode.  For one KV head, the pages of all sequences taken in order
+// (sequence 0's, then sequence 1's, ...) form one list of N pages, cut into
+// U = 4 * gridDim.x equal chunks of ppw = ceil(N / U) pages, one per wave.  A
+// chunk may hold the end of one sequence and the start of the next, so every
+// wave does the same amount of work whatever the mix of lengths.  A wave folds
+// each sequence it meets separately: a sequence that lies inside one chunk is
+// finished there (output row and logsumexp written directly); otherwise each
+// chunk that meets it writes a normalised partial, into slot chunk + sequence
+// of the KV head's U + B slots (unique: a chunk meeting sequence b+1 has
+// passed sequence b), and decode_bal_merge_kernel combines them.
+// Pages are counted from key_begin / 16 (the shared-prefix suffix pass).
+
+// Pages of sequence b past key_begin (0 when the sequence is shorter).
+__device__ __forceinline__ int bal_pages(const AttnArgs& a, int b, int pg0) {
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  return max(0, (ctx + kPage - 1) / kPage - pg0);
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += lane >= o ? y : 0;
+  }
+  return x;
+}
+
+// Pages per chunk, from the total page count of all sequences.  The first
+// 64 sequences' counts are returned in n0 (lane j: sequence j).
+__device__ __forceinline__ int bal_chunk_pages(const AttnArgs& a, int U, int pg0, int lane,
+                                               int& n0) {
+  int N = 0;
+  n0 = 0;
+  for (int k0 = 0; k0 < a.num_seqs; k0 += 64) {
+    const int n = k0 + lane < a.num_seqs ? bal_pages(a, k0 + lane, pg0) : 0;
+    if (k0 == 0) n0 = n;
+    N += wave_sum_i32(n);
+  }
+  N = __builtin_amdgcn_readfirstlane(N);
+  return (N + U - 1) / U;
+}
+
+template <int D, bool FP8, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
+void decode_bal_kernel(AttnArgs a) {
+  const int g = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c = lane & 15, grp = lane >> 4;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, B = a.num_seqs;
+  const int U = gridDim.x * kWaves, u = blockIdx.x * kWaves + wave;
+  const int pg0 = a.key_begin / kPage;
+  const float sc = a.scale * kLog2e;
+
+  int n0;
+  const int ppw = bal_chunk_pages(a, U, pg0, lane, n0);
+  if (ppw == 0) return;
+  const int c0 = u * ppw, c1 = c0 + ppw;  // this wave's chunk [c0, c1) of the page list
+
+  int base = 0;  // pages of the sequences before k0
+  for (int k0 = 0; k0 < B; k0 += 64) {
+    if (base >= c1) break;
+    const int n = k0 == 0 ? n0 : (k0 + lane < B ? bal_pages(a, k0 + lane, pg0) : 0);
+    const int incl = wave_incl_scan(n, lane), excl = incl - n;
+    // sequences of this block that overlap the chunk
+    uint64_t meet = __ballot(n > 0 && base + excl < c1 && base + incl > c0);
+    while (meet) {
+      const int j = __builtin_ctzll(meet);
+      meet &= meet - 1;
+      const int b = k0 + j;
+      const int sb = base + __builtin_amdgcn_readlane(excl, j);
+      const int nb = __builtin_amdgcn_readlane(n, j);
+      const int lp0 = max(c0, sb) - sb, lp1 = min(c1, sb + nb) - sb;
+      const bool whole = sb / ppw == (sb + nb - 1) / ppw;
+      int ctx = a.ctx_lens[b];
+      ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+
+      bf16x8 qf[D / 32];
+      load_q<D>(qf, a, b, g, G, c, grp);
+      DecodeState<D> st;
+      const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride + pg0 + lp0;
+      KVFrag<D> ring[kRing];
+      for (int i0 = 0; i0 < lp1 - lp0; i0 += 64) {
+        const int np = min(64, lp1 - lp0 - i0);
+        const int32_t my_id = lane < np ? bt[i0 + lane] : -1;
+        auto id_at = [&](int i) -> int32_t {
+          return i < np ? __builtin_amdgcn_readlane(my_id, min(i, 63)) : -1;
+        };
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) load_page<D, FP8, NT>(ring[r], a, id_at(r), g, lane);
+        for (int i = 0; i < np; i += kRing) {
+#pragma unroll
+          for (int r = 0; r < kRing; ++r) {
+            if (valid_block(id_at(i + r), a.num_blocks))
+              fold_page<D, FP8>(st, ring[r], qf, pg0 + lp0 + i0 + i + r, ctx, sc, grp);
+            load_page<D, FP8, NT>(ring[r], a, id_at(i + r + kRing), g, lane);
+          }
+        }
+      }
+
+      const float l = sum_xor32(sum_xor16(st.l));
+      const bool empty = !(l > 0.f);
+      const float inv = empty ? 0.f : 1.f / l;
+      const float lse = empty ? -INFINITY : (st.m + __log2f(l)) * kLn2;
+      if (c < G) {
+        const int64_t row = static_cast<int64_t>(b) * Hq + g * G + c;
+        if (whole) {
+          uint16_t* op = static_cast<uint16_t*>(a.o) + row * D + grp * 4;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) {
+            u32x2 w;
+            w.x = pack_bf16x2(st.acc[db][0] * inv, st.acc[db][1] * inv);
+            w.y = pack_bf16x2(st.acc[db][2] * inv, st.acc[db][3] * inv);
+            *reinterpret_cast<u32x2*>(op + db * 16) = w;
+          }
+          if (grp == 0 && a.lse) a.lse[row] = lse;
+        } else {
+          const int64_t prow = (static_cast<int64_t>(g) * (U + B) + u + b) * G + c;
+          float* op = a.ws_o + prow * D + grp * 4;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(op + db * 16) = st.acc[db] * inv;
+          if (grp == 0) a.ws_lse[prow] = lse;
+        }
+      }
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
+// Merge of the balanced decode's partials: one wave per (sequence, query
+// head).  Sequences that lie inside one chunk were finished by the decode
+// kernel; a sequence with no pages gets a zero row and lse = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void decode_bal_merge_kernel(AttnArgs a, int U) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, B = a.num_seqs;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (row >= static_cast<int64_t>(B) * Hq) return;
+  const int b = static_cast<int>(row / Hq), h = static_cast<int>(row % Hq);
+  const int g = h / G, c = h % G;
+  const int pg0 = a.key_begin / kPage;
+  int n0;
+  const int ppw = bal_chunk_pages(a, U, pg0, lane, n0);
+  // first page sb and page count nb of sequence b in the list
+  int sb = 0, nb = 0;
+  for (int k0 = 0; k0 < B; k0 += 64) {
+    const int n = k0 == 0 ? n0 : (k0 + lane < B ? bal_pages(a, k0 + lane, pg0) : 0);
+    if (b < k0 + 64) {
+      const int j = b - k0;
+      sb += wave_sum_i32(lane < j ? n : 0);
+      nb = __builtin_amdgcn_readlane(n, j);
+      break;
+    }
+    sb += wave_sum_i32(n);
+  }
+  constexpr int NPL = D / 64;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + row * D + lane;
+  if (nb == 0) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) orow[64 * j] = 0;
+    if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
+    return;
+  }
+  const int u0 = sb / ppw, u1 = (sb + nb - 1) / ppw;
+  if (u0 == u1) return;
+  const int S = u1 - u0 + 1;
+  const int64_t p0 = (static_cast<int64_t>(g) * (U + B) + u0 + b) * G + c;  // slot u0 + b
+  // partial s of this row: p0 + s * G
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, a.ws_lse[p0 + static_cast<int64_t>(s) * G]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float acc[NPL] = {};
+  float W = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    const float lt = s < S ? a.ws_lse[p0 + static_cast<int64_t>(s) * G] : -INFINITY;
+    const float w = lt == -INFINITY ? 0.f : fast_exp2((lt - Mu) * kLog2e);
+    W += w;
+    const int n = min(64, S - s0);
+    const float* op = a.ws_o + (p0 + static_cast<int64_t>(s0) * G) * D + lane;
+    const int wbits = __builtin_bit_cast(int, w);
+    int k = 0;
+    for (; k + 8 <= n; k += 8) {  // 8 partials' loads in flight at once
+      float x[8][NPL];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) x[q][j] = op[static_cast<int64_t>(k + q) * G * D + 64 * j];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, k + q));
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) acc[j] += wk * x[q][j];
+      }
+    }
+    for (; k < n; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, k));
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[j] += wk * op[static_cast<int64_t>(k) * G * D + 64 * j];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) W += __shfl_xor(W, o);
+  const bool empty = !(W > 0.f);
+  const float inv = empty ? 0.f : 1.f / W;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) orow[64 * j] = to_bf16_bits(acc[j] * inv);
+  if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : M + __logf(W);
 }
 
 // fp32 pools: one wave per (query head, sequence, page range), 64 keys per
@@ -429,8 +666,32 @@ hipError_t launch_split_d(const AttnArgs& a, hipStream_t st) {
 }
 
 template <int D>
+hipError_t launch_balanced_d(const AttnArgs& a, hipStream_t st) {
+  const int wgs = balanced_wgs(a.num_seqs, a.num_kv_heads, a.max_ctx_len, a.key_begin);
+  const dim3 grid(wgs, a.num_kv_heads);
+  const double es = a.kv_dtype == PA_FP8_E4M3 ? 1.0 : 2.0;
+  const double max_bytes = 2.0 * es * D * a.num_kv_heads * static_cast<double>(a.num_seqs) *
+                           (a.max_ctx_len - a.key_begin);
+  const bool nt = max_bytes > 512.0 * (1 << 20);
+  if (a.kv_dtype == PA_FP8_E4M3) {
+    if (nt) decode_bal_kernel<D, true, true><<<grid, 256, 0, st>>>(a);
+    else decode_bal_kernel<D, true, false><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (nt) decode_bal_kernel<D, false, true><<<grid, 256, 0, st>>>(a);
+    else decode_bal_kernel<D, false, false><<<grid, 256, 0, st>>>(a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  decode_bal_merge_kernel<D><<<static_cast<unsigned>((rows + kWaves - 1) / kWaves), 256, 0, st>>>(
+      a, 4 * wgs);
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
   const int S = a.num_splits;
+  if (S < 0) return launch_balanced_d<D>(a, st);
   if (a.kv_dtype == PA_F32) {
     const dim3 grid(S, (a.num_q_heads + kWaves - 1) / kWaves, a.num_seqs);
     decode_f32_kernel<D><<<grid, 256, 0, st>>>(a);

@@ -144,6 +144,11 @@ __device__ __forceinline__ float wave_max(float x) {
   for (int s = 1; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
   return x;
 }
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s);
+  return x;
+}
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s);
@@ -219,6 +224,27 @@ __device__ __forceinline__ void f32_attend(const AttnArgs& a, const int32_t* bt,
       }
     }
   }
+}
+
+// Workgroups per KV head of the balanced decode (4 waves each): about 512 in
+// all (two per compute unit), and no more waves than half the pages.
+inline int balanced_wgs(int num_seqs, int num_kv_heads, int max_ctx_len, int key_begin) {
+  const int64_t per_seq = (max_ctx_len + 15) / 16 - key_begin / 16;
+  const int64_t pages = static_cast<int64_t>(num_seqs) * (per_seq > 0 ? per_seq : 0);
+  int64_t w = (512 + num_kv_heads - 1) / num_kv_heads;
+  const int64_t by_pages = (pages + 7) / 8;
+  if (w > by_pages) w = by_pages;
+  return static_cast<int>(w < 1 ? 1 : w);
+}
+// Workspace of the balanced decode: per KV head, U + B partial slots (U =
+// 4 * balanced_wgs waves) of G rows: fp32 rows of head_dim, then one lse each.
+inline size_t balanced_ws_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int max_ctx_len, int key_begin) {
+  const int64_t U = 4 * static_cast<int64_t>(
+                            balanced_wgs(num_seqs, num_kv_heads, max_ctx_len, key_begin));
+  const size_t rows = static_cast<size_t>(num_q_heads) * (U + num_seqs);
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return o_bytes + rows * sizeof(float);
 }
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t st);

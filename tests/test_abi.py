@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 3
+    assert pa.abi_version() == 4
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -145,7 +145,15 @@ def test_decode_workspace_checks():
     assert _decode(_FakePool(), ws=0) == pa.PA_ERR_WORKSPACE
     assert _decode(_FakePool(), ws=0x10000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
     assert _decode(_FakePool(), ws=0x10008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG
-    assert _decode(_FakePool(), splits=-1) == pa.PA_ERR_INVALID_ARG
+    assert _decode(_FakePool(), splits=-2) == pa.PA_ERR_INVALID_ARG
+    # balanced decode: its own workspace, none given
+    assert _decode(_FakePool(), splits=pa.DECODE_BALANCED, ws=0) == pa.PA_ERR_WORKSPACE
+    nb = pa.decode_balanced_workspace_bytes(2, 8, 2, 128, 64)
+    assert nb >= 8 * (4 * 1 + 2) * (128 + 1) * 4   # 64 tokens x 2 seqs -> one workgroup per head
+    assert _decode(_FakePool(), splits=pa.DECODE_BALANCED, ws=0x10000,
+                   ws_bytes=nb - 1) == pa.PA_ERR_WORKSPACE
+    assert _decode(_FakePool(kv_dtype=pa.PA_F32), q_dtype=pa.PA_F32, splits=pa.DECODE_BALANCED,
+                   ws=0x10000, ws_bytes=nb) == pa.PA_ERR_UNSUPPORTED
 
 
 def test_prefill_split_checks_and_heuristic():
@@ -201,8 +209,17 @@ def test_decode_split_heuristic():
     # long context, few sequences: many splits; short contexts: few
     assert pa.decode_num_splits(8, 8, 32768) == 8
     assert pa.decode_num_splits(1, 1, 100) == 1
-    assert 1 <= pa.decode_num_splits(32, 8, 2048) <= 16
+    # a workgroup per compute unit already: no split
+    assert pa.decode_num_splits(32, 8, 2048) == 1
+    assert pa.decode_num_splits(16, 8, 2048) == 4
     assert pa.decode_num_splits(0, 8, 100) == 1
+    # uneven batches go to the balanced kernel, even ones keep the split choice
+    assert pa.decode_choose_splits(32, 8, 32768, 32768 + 31 * 256) == pa.DECODE_BALANCED
+    assert pa.decode_choose_splits(64, 8, 8192, 4 * 8192 + 60 * 128) == pa.DECODE_BALANCED
+    assert pa.decode_choose_splits(32, 8, 2048, 32 * 1088) == 1
+    assert pa.decode_choose_splits(8, 8, 32768, 8 * 32768) == 8
+    assert pa.decode_choose_splits(8, 8, 32768, 0) == 8          # total unknown
+    assert pa.decode_choose_splits(1, 8, 5000, 10) == pa.decode_num_splits(1, 8, 5000)
 
 
 def test_write_kv_checks():

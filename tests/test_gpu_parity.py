@@ -250,6 +250,68 @@ def test_mixed_batch_in_one_prefill_call():
     assert (lse[rows] - ld).abs().max() <= 1e-3
 
 
+BALANCED_CASES = [
+    # kv, D, Hq, Hkv, ctx_lens
+    ("bf16", 128, 32, 8, (1, 15, 16, 17, 250, 513, 2048, 40, 900, 33)),   # mixed, ragged
+    ("bf16", 128, 8, 2, tuple(range(1, 700, 7))),                          # 100 sequences (> 64)
+    ("bf16", 64, 16, 1, (3000, 17, 45, 2)),
+    ("fp8", 128, 32, 8, (128, 2048, 1000, 129, 16, 700, 1536, 1)),
+    ("fp8", 64, 8, 8, (64, 65, 300)),
+    ("bf16", 128, 16, 16, (4096,)),                                        # one long sequence
+]
+
+
+@pytest.mark.parametrize("kv,D,Hq,Hkv,ctx", BALANCED_CASES)
+def test_balanced_decode_parity(kv, D, Hq, Hkv, ctx):
+    """Balanced decode (each KV head's pages of all sequences cut into equal
+    per-wave chunks that may span sequences) against the oracle; and equal to
+    the split decode within rounding."""
+    _log(f"balanced decode kv={kv} D={D} Hq={Hq} Hkv={Hkv} ctx={ctx[:12]}")
+    wl = workloads.small("decode", kv_dtype=kv, q_dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, ctx_lens=ctx, seed=70 + D + Hkv)
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    o, lse = _check_call(wl, wl.calls[0], pool, opool, num_splits=pa.DECODE_BALANCED)
+    o2, l2 = H.DeviceCall(wl, wl.calls[0]).run(pool, num_splits=1)
+    assert (o.float() - o2.float()).abs().max().item() <= H.tolerance(wl)
+    assert (lse - l2).abs().max().item() <= 1e-3
+    # bitwise repeatable
+    o3, l3 = H.DeviceCall(wl, wl.calls[0]).run(pool, num_splits=pa.DECODE_BALANCED)
+    assert torch.equal(o, o3) and torch.equal(lse, l3)
+
+
+def test_decode_auto_choice_on_uneven_batch():
+    """With the batch's total length known, a batch whose longest sequence is
+    far above the mean is routed to the balanced kernel and still matches."""
+    _log("decode auto choice, uneven batch")
+    ctx = (3000,) + (40,) * 20 + (17, 1)
+    wl = workloads.small("decode", kv_dtype="bf16", q_dtype="bf16", num_q_heads=16,
+                         num_kv_heads=4, head_dim=128, ctx_lens=ctx, seed=77)
+    assert pa.decode_choose_splits(len(ctx), 4, 3000, sum(ctx)) == pa.DECODE_BALANCED
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    call = wl.calls[0]
+    dc = H.DeviceCall(wl, call)
+    o, lse = pa.decode(pool, dc.q, dc.ctx_lens, dc.block_table, wl.scale, max_ctx_len=3000,
+                       total_ctx_len=sum(ctx))
+    torch.cuda.synchronize()
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    _log(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= H.TOL["bf16"] and el <= H.TOL["bf16"]
+    o2, l2 = pa.decode(pool, dc.q, dc.ctx_lens, dc.block_table, wl.scale,
+                       num_splits=pa.DECODE_BALANCED)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_balanced_decode_named_full():
+    """The 32-sequence mixed-length and 8 x 32768 decode workloads, balanced."""
+    for k in (2, 4):
+        _log(f"balanced decode, named workload {k}")
+        wl, opool = _named(k)
+        pool = H.device_pool(wl)
+        call = [c for c in wl.calls if c.kind == "decode"][0]
+        _check_call(wl, call, pool, opool, num_splits=pa.DECODE_BALANCED)
+
+
 # ------------------------------------------------------------ shared prefix
 def _run_shared(wl, call, pool, prefix, **kw):
     dc = H.DeviceCall(wl, call)
