@@ -238,6 +238,70 @@ def bench_append(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_shared_prefix_decode(args):
+    """64 decode rows over a shared 4096-token prefix (+512 own tokens each):
+    pa_decode against pa_prefill_shared_prefix, each timed alone with the
+    last-level cache evicted before every step.  The metric is the logical
+    K/V bytes the step attends over (what pa_decode reads) per second."""
+    import torch
+    import online_softmax_paged_amd as pa
+    import workloads
+    dev = torch.device("cuda:0")
+    wl = workloads.shared_prefix_decode_bf16()
+    pool = pa.KVPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, device=dev)
+    pa.write_kv(pool, wl.k_src.to(dev), wl.v_src.to(dev), wl.slot_mapping.to(dev))
+    call = wl.calls[0]
+    q = call.q.to(dev)
+    ctx, bt = call.ctx_lens.to(dev), call.block_table.to(dev)
+    cu = torch.arange(q.shape[0] + 1, dtype=torch.int32, device=dev)
+    B, Hq, D = q.shape
+    mc, P = int(call.ctx_lens.max()), wl.shared_prefix
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    S = pa.decode_choose_splits(B, wl.num_kv_heads, mc, int(call.ctx_lens.sum()))
+    ws = torch.empty(max(1, pa.decode_workspace_bytes(B, Hq, D, S)), dtype=torch.uint8, device=dev)
+    sp, ss = pa.shared_prefix_num_splits(B, wl.num_kv_heads, Hq, 1, mc, P, B)
+    ws2 = torch.empty(pa.shared_prefix_workspace_bytes(B, Hq, D, sp + ss), dtype=torch.uint8,
+                      device=dev)
+    fns = {
+        "decode": lambda: pa.decode(pool, q, ctx, bt, wl.scale, max_ctx_len=mc, num_splits=S,
+                                    workspace=ws, out=o, lse=lse),
+        "shared_prefix": lambda: pa.prefill_shared_prefix(
+            pool, q, cu, ctx, bt, wl.scale, P, max_q_len=1, max_ctx_len=mc, out=o, lse=lse,
+            prefix_splits=sp, suffix_splits=ss, workspace=ws2),
+    }
+    scratch = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    logical = decode_kv_bytes(call, wl)
+    unique = 2.0 * wl.num_kv_heads * D * 2 * (P + B * (mc - P))
+    times = {}
+    for name, fn in fns.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(args.steps):
+            scratch.sum(dtype=torch.int64)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        times[name] = tot / args.steps
+    ms = times["shared_prefix"]
+    result = {"metric": "decode over a shared prefix: logical KV GB/s", "value": logical / (ms * 1e-3) / 1e9,
+              "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)",
+              "config": {"workload": wl.name, "cache_flush_mb": 512},
+              "parts": {"decode_ms": times["decode"], "shared_prefix_ms": ms,
+                        "speedup": times["decode"] / ms, "logical_kv_bytes": logical,
+                        "unique_kv_bytes": unique, "decode_splits": S,
+                        "shared_prefix_splits": [sp, ss],
+                        "unique_gbps": unique / (ms * 1e-3) / 1e9}}
+    print(json.dumps(result), flush=True)
+
+
 def one_call_timings(pa, wl, pool, dev, args, scratch):
     """The workload's calls (chunks and decode rows) as ONE varlen call, timed
     two ways after the main loop: pa_prefill, and pa_prefill_shared_prefix
@@ -300,6 +364,9 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="MB of scratch written between steps to evict the 256 MB last-level "
                          "cache (-1 = 512 when a decode call reads less than 512 MB of KV)")
+    ap.add_argument("--one-call", action="store_true",
+                    help="also time a shared-prefix workload's calls joined into one call "
+                         "(pa_prefill and pa_prefill_shared_prefix), outside the step")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB after the "
                          "warmup (outside the timed region) to calibrate HBM byte counters")
@@ -330,6 +397,9 @@ def main():
 
     if args.workload == "append":
         bench_append(args)
+        return
+    if args.workload == "shared":
+        bench_shared_prefix_decode(args)
         return
     if args.workload == "headline":
         wls = [workloads.causal_prefill_bf16(), workloads.long_decode_bf16()]
@@ -457,9 +527,10 @@ def main():
         result["decode"] = {"value": sum(x["kv_bytes"] for x in dec) / (sum(x["ms"] for x in dec) * 1e-3) / 1e9,
                             "unit": "GB/s", "frac_hbm_peak": None}
         result["decode"]["frac_hbm_peak"] = result["decode"]["value"] / PEAK_HBM_GBPS
-    for wl in wls:
-        if wl.shared_prefix and len(wl.calls) > 1:
-            parts["one_call"] = one_call_timings(pa, wl, pools[wl.name], dev, args, scratch)
+    if args.one_call:
+        for wl in wls:
+            if wl.shared_prefix and len(wl.calls) > 1:
+                parts["one_call"] = one_call_timings(pa, wl, pools[wl.name], dev, args, scratch)
     result["parts"] = parts
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wls, args.cpu_budget)

@@ -32,11 +32,15 @@ namespace {
 
 constexpr int kWaves = 4;
 #ifndef PA_DECODE_RING
-#define PA_DECODE_RING 3
+#define PA_DECODE_RING 2
 #endif
-// Pages in flight per wave.  Measured (batched 32 x 128..2048 / long 8 x
-// 32768 / fp8 mixed): 3 pages 42.1 / 173.3 / 19.0 us, 4 pages 41.9 / 172.5 /
-// 20.7 us, 5 pages 44.7 / 173.8 / 22.7 us.
+// Pages in flight per wave.  Two pages keep the split kernel within 168
+// VGPRs, so three workgroups fit per compute unit instead of two.  Measured
+// (batched 32 x 128..2048 / long 8 x 32768 / fp8 mixed / 64 x 512, split
+// heuristic of the time): 2 pages at 3 waves per SIMD 41.0 / 171.1 / 19.1 /
+// 29.5 us; 3 pages at 2 waves per SIMD 42.8 / 172.4 / 19.5 / 30.8 us; 3 pages
+// at 3 waves per SIMD 42.3 / 172.1 / 33.1 (fp8 spills) / 30.0 us; 4 and 5
+// pages at 2 waves per SIMD no faster than 3.
 constexpr int kRing = PA_DECODE_RING;
 
 template <int D>
@@ -186,7 +190,7 @@ __device__ __forceinline__ void fold_page(DecodeState<D>& st, KVFrag<D>& f,
 }
 
 #ifndef PA_DECODE_WAVES_PER_EU
-#define PA_DECODE_WAVES_PER_EU 2
+#define PA_DECODE_WAVES_PER_EU 3
 #endif
 
 template <int D, bool FP8, bool NT>

@@ -233,6 +233,15 @@ def mixed_fp8() -> Workload:
                         Call("decode", list(range(8, 16)), [1] * 8)], seed=1005)
 
 
+def shared_prefix_decode_bf16() -> Workload:
+    """64 sequences that share a 4096-token prefix and hold 512 own tokens
+    each (4608 in all), one decode query each; 32 q / 8 KV heads, d=128."""
+    return build("shared_prefix_decode_bf16_64x4608_prefix4096_gqa4_d128", kv_dtype="bf16",
+                 q_dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 ctx_lens=[4608] * 64, shared_prefix=4096,
+                 calls=[Call("decode", list(range(64)), [1] * 64)], seed=1006)
+
+
 NAMED = {
     1: tiny_fp32,
     2: batched_decode_bf16,
