@@ -22,11 +22,17 @@ the attention mathematics):
                    blocks with reference counts, copy on write before a
                    sequence writes into a shared block (the PagedAttention
                    section of the survey page).
+* ``backward``  -- the gradients dQ, dK, dV of the same attention for an
+                   upstream dO: the chain rule through the softmax written out
+                   with the full probability matrix (the pages describe the
+                   backward only as recomputation from kept statistics).
 
-Every function is pinned by the ``-m "not gpu"`` tests in tests/test_oracle.py
-(brute force, closed forms, library special cases and invariants).
+Every function is pinned by the ``-m "not gpu"`` tests in tests/test_oracle.py,
+tests/test_blocks.py and tests/test_oracle_backward.py (brute force, closed
+forms, finite differences, library special cases and invariants).
 """
-from . import fp8_e4m3, pool, attention, blocks  # noqa: F401
+from . import fp8_e4m3, pool, attention, blocks, backward  # noqa: F401
 from .pool import OraclePool, write_kv, append_kv, copy_blocks, gather_kv  # noqa: F401
 from .attention import (attention_two_pass, paged_attention, paged_attention_rows,  # noqa: F401
                         online_softmax_pages, lse_merge)
+from .backward import attention_backward_dense, paged_attention_backward  # noqa: F401
