@@ -238,6 +238,55 @@ def bench_append(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_backward(args):
+    """Backward of the causal prefill 4 x 4096 (32 q / 8 KV heads, d=128,
+    bf16): dQ, dK, dV from the forward's o and lse.  FLOPs are the usual five
+    products per visible (query, key, head) -- Q K^T, dO V^T, P^T dO, dS^T Q,
+    dS K -- 2.5 times the forward's; the kernels compute Q K^T and dO V^T
+    twice (once for dK/dV, once for dQ), 7 products in all."""
+    import torch
+    import online_softmax_paged_amd as pa
+    import workloads
+    dev = torch.device("cuda:0")
+    wl = workloads.causal_prefill_bf16()
+    pool = pa.KVPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, device=dev)
+    pa.write_kv(pool, wl.k_src.to(dev), wl.v_src.to(dev), wl.slot_mapping.to(dev))
+    call = wl.calls[0]
+    q = call.q.to(dev)
+    cu, ctx, bt = call.cu_q_lens.to(dev), call.ctx_lens.to(dev), call.block_table.to(dev)
+    mq, mc = max(call.q_lens), int(call.ctx_lens.max())
+    B, (T, Hq, D) = len(call.q_lens), q.shape
+    o, lse = pa.prefill(pool, q, cu, ctx, bt, wl.scale, max_q_len=mq, max_ctx_len=mc, num_splits=1)
+    do = workloads.upstream_grad(call, D, Hq, seed=2024).to(dev)
+    dq = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    dk = torch.zeros(pool.k.shape, dtype=torch.float32, device=dev)
+    dv = torch.zeros(pool.v.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(pa.backward_workspace_bytes(pool, B, Hq, mq), dtype=torch.uint8, device=dev)
+    fn = lambda: pa.prefill_backward(pool, q, o, lse, do, cu, ctx, bt, wl.scale, max_q_len=mq,
+                                     max_ctx_len=mc, dq=dq, dk=dk, dv=dv, workspace=ws)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = 2.5 * prefill_flops(call, D, Hq)
+    tf = fl / (ms * 1e-3) / 1e12
+    result = {"metric": "prefill backward TFLOP/s (5 products per visible pair)", "value": tf,
+              "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V/dO, shuffled pages)",
+              "config": {"workload": wl.name + " backward"},
+              "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tf / PEAK_BF16_TFLOPS, "traffic": None},
+              "parts": {"flops": fl, "products_computed": 7}}
+    print(json.dumps(result), flush=True)
+
+
 def bench_shared_prefix_decode(args):
     """64 decode rows over a shared 4096-token prefix (+512 own tokens each):
     pa_decode against pa_prefill_shared_prefix, each timed alone with the
@@ -400,6 +449,9 @@ def main():
         return
     if args.workload == "shared":
         bench_shared_prefix_decode(args)
+        return
+    if args.workload == "backward":
+        bench_backward(args)
         return
     if args.workload == "headline":
         wls = [workloads.causal_prefill_bf16(), workloads.long_decode_bf16()]

@@ -200,6 +200,41 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
                      float scale, int32_t causal, int32_t num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ backward
+ * Gradients of pa_prefill's attention for an upstream gradient dout, from the
+ * forward's output o and logsumexp lse: the attention weights are recomputed
+ * tile by tile instead of stored (the FlashAttention page, core-principle
+ * section: the backward rebuilds them from the kept statistics).  With
+ * P = softmax(scale Q K^T) (masked as the forward masks it):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV summed over the G query heads of each KV head.
+ *   q, o, dout : [cu_q_lens[num_seqs], num_q_heads, head_dim] bf16 (device)
+ *   lse        : float [cu_q_lens[num_seqs], num_q_heads], as pa_prefill wrote it
+ *   dq         : float [cu_q_lens[num_seqs], num_q_heads, head_dim] (written)
+ *   dk         : float, the K pool's shape [num_blocks, num_kv_heads, 16, head_dim]
+ *   dv         : float, the V pool's shape [num_blocks, num_kv_heads, head_dim, 16]
+ * Every slot of every page a sequence uses is written (slots at or past its
+ * context length with 0); other pages are not touched.  Other arguments as
+ * pa_prefill.  Supported: bf16 pools with bf16 q, head_dim 64 or 128.
+ * Device-resident contract (not checked): no physical page is used by two
+ * sequences (their gradients would race) or twice by one.
+ * workspace: pa_backward_workspace_bytes(pool, num_seqs, num_q_heads,
+ *   max_q_len) bytes of device memory, 16-byte aligned, contents need not be
+ *   initialised (transposed copies of Q, dO and the used pages, rowsum(dO*O)
+ *   and lse per query row).  dout, dq, dk, dv 16-byte aligned.
+ */
+size_t pa_backward_workspace_bytes(const pa_kv_pool* pool, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_q_len);
+pa_status pa_prefill_backward(const pa_kv_pool* pool, const void* q, const void* o,
+                              const float* lse, const void* dout, pa_dtype q_dtype, float* dq,
+                              float* dk, float* dv, const int32_t* cu_q_lens,
+                              const int32_t* ctx_lens, const int32_t* block_table,
+                              int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_q_len, int32_t max_ctx_len, float scale,
+                              int32_t causal, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* ------------------------------------------------------------ shared prefix
  * pa_prefill for a batch whose sequences all begin with the same prefix_len
  * tokens held in the same physical blocks (reference-counted sharing of a

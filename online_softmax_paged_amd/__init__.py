@@ -62,6 +62,10 @@ _sp_ws = _sig("pa_shared_prefix_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
 _prefill_sp = _sig("pa_prefill_shared_prefix", ctypes.c_int,
                    [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                     _F, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP])
+_bwd_ws = _sig("pa_backward_workspace_bytes", _SZ, [_P, _I32, _I32, _I32])
+_bwd = _sig("pa_prefill_backward", ctypes.c_int,
+            [_P, _VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
+             _I32, _I32, _F, _I32, _VP, _SZ, _VP])
 _num_splits = _sig("pa_decode_num_splits", _I32, [_I32, _I32, _I32])
 _choose_splits = _sig("pa_decode_choose_splits", _I32, [_I32, _I32, _I32, ctypes.c_int64])
 _dec_ws = _sig("pa_decode_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
@@ -88,7 +92,8 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_append_kv", "pa_copy_blocks", "pa_plan_append", "pa_prefill_num_splits",
             "pa_prefill_workspace_bytes", "pa_shared_prefix_num_splits",
             "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
-            "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits"]
+            "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits",
+            "pa_backward_workspace_bytes", "pa_prefill_backward"]
 
 DECODE_BALANCED = -1
 
@@ -348,6 +353,52 @@ def prefill_shared_prefix(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, bl
                        suffix_splits, _ptr(workspace), workspace.numel(), _stream(stream)),
            "pa_prefill_shared_prefix")
     return o, lse
+
+
+def backward_workspace_bytes(pool: KVPool, num_seqs: int, num_q_heads: int,
+                             max_q_len: int) -> int:
+    return int(_bwd_ws(pool.c, num_seqs, num_q_heads, max_q_len))
+
+
+def prefill_backward(pool: KVPool, q: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                     dout: torch.Tensor, cu_q_lens, ctx_lens, block_table, scale: float,
+                     causal: bool = True, max_q_len: int | None = None,
+                     max_ctx_len: int | None = None, dq: torch.Tensor | None = None,
+                     dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, validate: bool = False,
+                     stream=None):
+    """Gradients of prefill() for the upstream gradient dout, from its o and
+    lse.  Returns (dq [T, Hq, d], dk shaped like pool.k, dv shaped like
+    pool.v), all float32; dk and dv are zero on pages no sequence uses
+    (allocated zeroed here when not given)."""
+    B = int(ctx_lens.numel())
+    T, Hq, D = q.shape
+    if max_q_len is None or max_ctx_len is None or validate:
+        cu = cu_q_lens.cpu()
+        q_lens = (cu[1:] - cu[:-1]).tolist()
+        if max_q_len is None:
+            max_q_len = max(q_lens) if q_lens else 0
+        if max_ctx_len is None:
+            max_ctx_len = int(ctx_lens.max().item()) if B else 0
+        if validate:
+            _validate(pool, ctx_lens, block_table, q_lens)
+            bt, cl = block_table.cpu(), ctx_lens.cpu().tolist()
+            used = [int(x) for b in range(B) for x in bt[b, :(cl[b] + 15) // 16].tolist()]
+            if len(used) != len(set(used)):
+                raise ValueError("a physical page is used twice: its gradient would race")
+    dq = dq if dq is not None else torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    dk = dk if dk is not None else torch.zeros(pool.k.shape, dtype=torch.float32, device=q.device)
+    dv = dv if dv is not None else torch.zeros(pool.v.shape, dtype=torch.float32, device=q.device)
+    if B == 0:
+        return dq, dk, dv
+    need = backward_workspace_bytes(pool, B, Hq, max_q_len)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(_bwd(pool.c, _ptr(q), _ptr(o), _ptr(lse), _ptr(dout), _DT[q.dtype], _ptr(dq), _ptr(dk),
+                _ptr(dv), _ptr(cu_q_lens), _ptr(ctx_lens), _ptr(block_table), block_table.shape[1],
+                B, Hq, max_q_len, max_ctx_len, scale, 1 if causal else 0, _ptr(workspace),
+                workspace.numel(), _stream(stream)), "pa_prefill_backward")
+    return dq, dk, dv
 
 
 def decode_num_splits(num_seqs: int, num_kv_heads: int, max_ctx_len: int) -> int:

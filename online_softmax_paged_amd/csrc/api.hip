@@ -91,7 +91,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 4; }
+int32_t pa_abi_version(void) { return 5; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
@@ -307,6 +307,71 @@ pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dty
   a.part_rows = num_q_tokens;
   return launched(launch_prefill_shared_prefix(a, prefix_len, num_q_tokens, prefix_splits,
                                                suffix_splits, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_backward_workspace_bytes(const pa_kv_pool* pool, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_q_len) {
+  if (check_pool(pool) != PA_OK || num_seqs < 1 || max_q_len < 1 ||
+      num_q_heads < pool->num_kv_heads || num_q_heads % pool->num_kv_heads != 0)
+    return 0;
+  return backward_layout(num_seqs, max_q_len, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                         pool->num_blocks)
+      .total;
+}
+
+pa_status pa_prefill_backward(const pa_kv_pool* pool, const void* q, const void* o,
+                              const float* lse, const void* dout, pa_dtype q_dtype, float* dq,
+                              float* dk, float* dv, const int32_t* cu_q_lens,
+                              const int32_t* ctx_lens, const int32_t* block_table,
+                              int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_q_len, int32_t max_ctx_len, float scale,
+                              int32_t causal, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (num_seqs == 0 && pool) return check_pool(pool);
+  pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
+                           num_q_heads, max_ctx_len, scale);
+  if (s != PA_OK) return s;
+  if (pool->kv_dtype != PA_BF16 || q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!lse || !dout || !dq || !dk || !dv || !cu_q_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return PA_ERR_INVALID_ARG;
+  if (max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
+  const BwdLayout L = backward_layout(num_seqs, max_q_len, num_q_heads, pool->num_kv_heads,
+                                      pool->head_dim, pool->num_blocks);
+  if (!workspace || workspace_bytes < L.total) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  BwdArgs a{};
+  a.k = static_cast<const uint16_t*>(pool->k);
+  a.v = static_cast<const uint16_t*>(pool->v);
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.q = static_cast<const uint16_t*>(q);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu_q_lens = cu_q_lens;
+  a.ctx_lens = ctx_lens;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_q_len = max_q_len;
+  a.max_ctx_len = max_ctx_len;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  a.lpad = L.lpad;
+  char* w = static_cast<char*>(workspace);
+  a.qt = reinterpret_cast<uint16_t*>(w + L.off[0]);
+  a.dot = reinterpret_cast<uint16_t*>(w + L.off[1]);
+  a.delta = reinterpret_cast<float*>(w + L.off[2]);
+  a.lse2 = reinterpret_cast<float*>(w + L.off[3]);
+  a.kfm = reinterpret_cast<uint16_t*>(w + L.off[4]);
+  a.vtm = reinterpret_cast<uint16_t*>(w + L.off[5]);
+  return launched(launch_backward(a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pa_decode_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx_len) {

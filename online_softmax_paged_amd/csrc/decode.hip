@@ -696,13 +696,14 @@ template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
   const int S = a.num_splits;
   if (S < 0) return launch_balanced_d<D>(a, st);
+  hipError_t e;
   if (a.kv_dtype == PA_F32) {
     const dim3 grid(S, (a.num_q_heads + kWaves - 1) / kWaves, a.num_seqs);
     decode_f32_kernel<D><<<grid, 256, 0, st>>>(a);
+    e = hipGetLastError();
   } else {
-    launch_split_d<D>(a, st);
+    e = launch_split_d<D>(a, st);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
   const unsigned blocks = static_cast<unsigned>((rows + kWaves - 1) / kWaves);

@@ -247,6 +247,64 @@ inline size_t balanced_ws_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
   return o_bytes + rows * sizeof(float);
 }
 
+// Arguments of the backward kernels (bf16 pool, q, o, dO; fp32 gradients).
+struct BwdArgs {
+  const uint16_t* k;        // pool K [NB, Hkv, 16, D]
+  const uint16_t* v;        // pool V [NB, Hkv, D, 16]
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  const uint16_t* q;        // [T, Hq, D]
+  const uint16_t* o;        // forward output [T, Hq, D]
+  const float* lse;         // forward logsumexp [T, Hq]
+  const uint16_t* dout;     // upstream gradient [T, Hq, D]
+  float* dq;                // [T, Hq, D]
+  float* dk;                // [NB, Hkv, 16, D]
+  float* dv;                // [NB, Hkv, D, 16]
+  const int32_t* cu_q_lens;
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t max_q_len;
+  int32_t max_ctx_len;
+  float scale;
+  int32_t causal;
+  int32_t lpad;             // query rows per (KV head, sequence) in the row workspaces
+  uint16_t* qt;             // Q^T  [Hkv][D][B][lpad]
+  uint16_t* dot;            // dO^T [Hkv][D][B][lpad]
+  float* delta;             // rowsum(dO * O) [Hkv][B][lpad]
+  float* lse2;              // lse * log2(e)  [Hkv][B][lpad]
+  uint16_t* kfm;            // K pages feature-major [NB, Hkv, D, 16]
+  uint16_t* vtm;            // V pages token-major   [NB, Hkv, 16, D]
+};
+
+// Workspace of the backward: the six regions of BwdArgs, each 256-byte aligned.
+struct BwdLayout {
+  int lpad;
+  size_t off[6];  // qt, dot, delta, lse2, kfm, vtm
+  size_t total;
+};
+inline BwdLayout backward_layout(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int num_blocks) {
+  BwdLayout L;
+  const int G = num_q_heads / num_kv_heads;
+  L.lpad = ((max_q_len * G + 31) / 32) * 32;
+  const size_t rows = static_cast<size_t>(num_kv_heads) * num_seqs * L.lpad;
+  const size_t pages = static_cast<size_t>(num_blocks) * num_kv_heads * 16 * head_dim;
+  const size_t sz[6] = {rows * head_dim * 2, rows * head_dim * 2, rows * 4, rows * 4,
+                        pages * 2, pages * 2};
+  size_t o = 0;
+  for (int i = 0; i < 6; ++i) {
+    L.off[i] = o;
+    o += (sz[i] + 255) & ~static_cast<size_t>(255);
+  }
+  L.total = o;
+  return L;
+}
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t st);
 // The decode split pass alone (bf16 or fp8 pool), partials as a's workspace says.
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t st);

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 4
+    assert pa.abi_version() == 5
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -203,6 +203,33 @@ def test_shared_prefix_checks():
     assert sp == 1 and ss == 1
     with pytest.raises(pa.PAError):
         pa.shared_prefix_num_splits(1, 8, 32, 1, 64, 64, 1)
+
+
+def _backward(pool, **kw):
+    a = dict(q=0x5000, o=0x6000, lse=0x7000, dout=0x8000, q_dtype=pa.PA_BF16, dq=0x9000,
+             dk=0xa000, dv=0xb000, cu=0xc000, ctx=0xd000, bt=0xe000, stride=4, B=2, Hq=8,
+             max_q=64, max_ctx=64, scale=0.1, causal=1, ws=0, ws_bytes=0)
+    a.update(kw)
+    return pa._bwd(pool.c, a["q"], a["o"], a["lse"], a["dout"], a["q_dtype"], a["dq"], a["dk"],
+                   a["dv"], a["cu"], a["ctx"], a["bt"], a["stride"], a["B"], a["Hq"], a["max_q"],
+                   a["max_ctx"], a["scale"], a["causal"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_checks():
+    p = _FakePool()
+    need = pa._bwd_ws(p.c, 2, 8, 64)
+    # Q^T and dO^T: 2 KV heads x 128 features x 2 sequences x 256 rows, bf16
+    assert need >= 2 * (2 * 128 * 2 * 256 * 2)
+    assert pa._bwd_ws(p.c, 0, 8, 64) == 0
+    assert _backward(_FakePool(kv_dtype=pa.PA_F32), q_dtype=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
+    assert _backward(_FakePool(kv_dtype=pa.PA_FP8_E4M3)) == pa.PA_ERR_UNSUPPORTED
+    assert _backward(p) == pa.PA_ERR_WORKSPACE
+    assert _backward(p, ws=0x100000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
+    for bad in (dict(lse=0), dict(dout=0), dict(dq=0), dict(dk=0), dict(dv=0), dict(cu=0),
+                dict(dq=0x9004), dict(dk=0xa008), dict(max_q=0), dict(max_q=65)):
+        assert _backward(p, ws=0x100000, ws_bytes=need, **bad) == pa.PA_ERR_INVALID_ARG, bad
+    assert _backward(p, ws=0x100008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG
+    assert _backward(p, B=0) == pa.PA_OK
 
 
 def test_decode_split_heuristic():

@@ -1,0 +1,102 @@
+"""GPU parity of the backward (dQ, dK, dV) against the float64 backward
+oracle, through the C ABI.  The forward's o and lse come from the library's
+own pa_prefill; the oracle recomputes everything from the same seeded Q, K,
+V and dO.
+
+Bar: max |g - g_ref| <= 2e-2 * max(1, max |g_ref|) for each of dQ, dK and dV
+(bf16 inputs; P and dS are rounded to bf16 before their MFMAs and O is the
+forward's bf16 output, each a relative 2^-9 per element -- the same rounding
+budget as the forward's 2e-2 bar, applied to the gradients' own scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import paged_attention_backward
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+pa = pytest.importorskip("online_softmax_paged_amd")
+
+REL = 2e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _run_backward(wl, call, seed, causal=True, **kw):
+    pool = H.device_pool(wl)
+    dc = H.DeviceCall(wl, call)
+    o, lse = pa.prefill(pool, dc.q, dc.cu_q_lens, dc.ctx_lens, dc.block_table, wl.scale,
+                        causal=causal, max_q_len=dc.max_q_len, max_ctx_len=dc.max_ctx_len,
+                        num_splits=1)
+    do = workloads.upstream_grad(call, wl.head_dim, wl.num_q_heads, seed)
+    dq, dk, dv = pa.prefill_backward(pool, dc.q, o, lse, do.cuda(), dc.cu_q_lens, dc.ctx_lens,
+                                     dc.block_table, wl.scale, causal=causal,
+                                     max_q_len=dc.max_q_len, max_ctx_len=dc.max_ctx_len,
+                                     validate=True, **kw)
+    torch.cuda.synchronize()
+    return do, dq, dk, dv
+
+
+def _check(wl, call, do, dq, dk, dv, causal=True):
+    ref_q, ref_k, ref_v = paged_attention_backward(H.oracle_pool(wl), call.q, do, call.cu_q_lens,
+                                                   call.ctx_lens, call.block_table,
+                                                   wl.num_q_heads, wl.scale, causal)
+    errs = {}
+    for name, got, ref in (("dQ", dq, ref_q), ("dK", dk, ref_k), ("dV", dv, ref_v)):
+        g = got.detach().cpu().to(torch.float64).numpy()
+        assert np.isfinite(g).all(), f"{name}: non-finite"
+        err = float(np.abs(g - ref).max())
+        bound = REL * max(1.0, float(np.abs(ref).max()))
+        errs[name] = (err, bound)
+        assert err <= bound, (name, err, bound)
+    _log("  " + " ".join(f"{k}: {e:.2e} (bar {b:.2e})" for k, (e, b) in errs.items()))
+
+
+BACKWARD_CASES = [
+    # D, Hq, Hkv, ctx_lens, q_lens (None = whole sequences), causal
+    (128, 8, 2, (100, 37, 300), None, True),
+    (128, 8, 2, (300, 129, 70, 16), (64, 1, 70, 5), True),     # chunks, a decode row, ragged tails
+    (128, 8, 2, (200, 45), (60, 45), False),
+    (64, 4, 4, (257, 33), None, True),                          # G = 1
+    (128, 16, 2, (150, 90), (150, 17), True),                   # G = 8
+    (64, 16, 1, (70,), None, True),                             # G = 16
+]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,ctx,ql,causal", BACKWARD_CASES)
+def test_backward_parity(D, Hq, Hkv, ctx, ql, causal):
+    _log(f"backward D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} q={ql} causal={causal}")
+    wl = workloads.small("prefill", kv_dtype="bf16", q_dtype="bf16", num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=D, ctx_lens=ctx, q_lens=ql, seed=110 + D + Hq,
+                         causal=causal)
+    call = wl.calls[0]
+    do, dq, dk, dv = _run_backward(wl, call, seed=7, causal=causal)
+    _check(wl, call, do, dq, dk, dv, causal)
+
+
+def test_backward_is_deterministic_and_reuses_its_workspace():
+    wl = workloads.small("prefill", kv_dtype="bf16", q_dtype="bf16", num_q_heads=8,
+                         num_kv_heads=2, head_dim=128, ctx_lens=(333, 80), q_lens=(100, 80),
+                         seed=121)
+    call = wl.calls[0]
+    ws = torch.full((1 << 26,), 0x7F, dtype=torch.uint8, device="cuda")
+    _, a_q, a_k, a_v = _run_backward(wl, call, seed=3, workspace=ws)
+    _, b_q, b_k, b_v = _run_backward(wl, call, seed=3, workspace=ws)
+    assert torch.equal(a_q, b_q) and torch.equal(a_k, b_k) and torch.equal(a_v, b_v)
+
+
+def test_backward_prefill_1x2048_sampled_against_oracle():
+    """One 2048-token causal sequence, 32 q / 8 KV heads, d=128: every
+    gradient against the oracle (a few seconds of float64 on the CPU)."""
+    _log("backward 1 x 2048")
+    wl = workloads.build("bwd_2048", kv_dtype="bf16", q_dtype="bf16", num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, ctx_lens=[2048],
+                         calls=[workloads.Call("prefill", [0], [2048])], seed=131)
+    call = wl.calls[0]
+    do, dq, dk, dv = _run_backward(wl, call, seed=5)
+    _check(wl, call, do, dq, dk, dv)

@@ -160,6 +160,16 @@ def build(name: str, *, kv_dtype: str, q_dtype: str, num_q_heads: int,
         seed=seed, shared_prefix=shared_prefix)
 
 
+def upstream_grad(call: Call, head_dim: int, num_q_heads: int, seed: int,
+                  dtype: str = "bf16") -> torch.Tensor:
+    """A seeded upstream gradient dO for a call's queries: [T, Hq, d] drawn
+    as float32 randn on its own generator and cast (nearest even) to dtype."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    T = int(call.cu_q_lens[-1])
+    return torch.randn((T, num_q_heads, head_dim), dtype=torch.float32,
+                       generator=g).to(_TORCH_DTYPES[dtype])
+
+
 def one_call(wl: Workload) -> Call:
     """The workload's calls joined into one varlen call: sequences and query
     tokens in call order (a decode query is a one-token chunk at the last
