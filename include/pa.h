@@ -216,7 +216,8 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
  *   dv         : float, the V pool's shape [num_blocks, num_kv_heads, head_dim, 16]
  * Every slot of every page a sequence uses is written (slots at or past its
  * context length with 0); other pages are not touched.  Other arguments as
- * pa_prefill.  Supported: bf16 pools with bf16 q, head_dim 64 or 128.
+ * pa_prefill.  Supported: bf16 pools with bf16 q, head_dim 64 or 128, and
+ * max_q_len * (num_q_heads / num_kv_heads) * head_dim < 2^30.
  * Device-resident contract (not checked): no physical page is used by two
  * sequences (their gradients would race) or twice by one.
  * workspace: pa_backward_workspace_bytes(pool, num_seqs, num_q_heads,

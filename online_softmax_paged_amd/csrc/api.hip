@@ -338,6 +338,9 @@ pa_status pa_prefill_backward(const pa_kv_pool* pool, const void* q, const void*
   if (max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
   const BwdLayout L = backward_layout(num_seqs, max_q_len, num_q_heads, pool->num_kv_heads,
                                       pool->head_dim, pool->num_blocks);
+  // a sequence's transposed rows are addressed with 32-bit offsets
+  if (static_cast<int64_t>(L.lpad) * pool->head_dim * 2 >= (int64_t{1} << 31))
+    return PA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < L.total) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
   BwdArgs a{};

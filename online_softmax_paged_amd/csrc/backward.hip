@@ -27,6 +27,8 @@
 //
 // Query rows of a KV head g are the (token, head) pairs of its G query heads,
 // row R = t * G + (h - g * G) within a sequence, as in the forward.
+#include <climits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -85,9 +87,24 @@ __device__ __forceinline__ int32_t page_id(const BwdArgs& a, int b, int page, in
   return p >= 0 && p < a.num_blocks ? p : -1;
 }
 
+// Workgroups are dealt to the 8 dies (each with its own L2) round robin by
+// linear id.  When the (sequence, KV head) pairs split evenly over the dies,
+// die k takes pairs k*P .. k*P+P-1 with all their tiles (tile index y from 0,
+// the longest first), so the workgroups of a pair share the die's L2.
+__device__ __forceinline__ void die_task(int& pair, int& y) {
+  const int n_pair = gridDim.x;
+  pair = blockIdx.x;
+  y = blockIdx.y;
+  if (n_pair % 8 == 0) {
+    const int lin = blockIdx.y * n_pair + blockIdx.x, P = n_pair / 8, j = lin / 8;
+    pair = (lin % 8) * P + j % P;
+    y = j / P;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prep 1: per (sequence, KV head, 64 query rows): D = rowsum(dO * O), LSE *
-// log2(e), and Q^T, dO^T into [Hkv][D][B][lpad] (rows past the sequence 0).
+// log2(e), and Q^T, dO^T into [Hkv][B][D][lpad] (rows past the sequence 0).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
@@ -135,7 +152,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
       wq[k] = static_cast<uint32_t>(sq[r * LD + d]) | (static_cast<uint32_t>(sq[(r + 1) * LD + d]) << 16);
       wd[k] = static_cast<uint32_t>(sd[r * LD + d]) | (static_cast<uint32_t>(sd[(r + 1) * LD + d]) << 16);
     }
-    const int64_t off = ((static_cast<int64_t>(g) * D + d) * B + b) * a.lpad + R;
+    const int64_t off = ((static_cast<int64_t>(g) * B + b) * D + d) * a.lpad + R;
     *reinterpret_cast<u32x4*>(a.qt + off) = wq;
     *reinterpret_cast<u32x4*>(a.dot + off) = wd;
   }
@@ -202,23 +219,30 @@ __global__ __launch_bounds__(256) void bwd_pages_kernel(BwdArgs a) {
 // 32w..32w+31 of them, K and V of its keys held as MFMA operands.  The query
 // tiles (32 rows) that see any of the keys are staged in LDS for all four
 // waves: Q and dO row-major, Q^T and dO^T feature-major, D and LSE*log2(e).
+// Staging is by buffer loads straight into LDS (dma16) into two stages, so
+// the next tile moves while one is multiplied: wave w moves one of the four
+// operand tiles (its lanes' source offsets chosen so that the linear LDS
+// writes land in the swizzled layout), waves 0 and 1 also the row statistics.
 template <int D>
 struct RowsStage {
   uint16_t q[kBT * D], d[kBT * D], qt[kBT * D], dt[kBT * D];
-  float lse2[kBT], delta[kBT];
+  float lse2[256], delta[256];  // one 1 KiB load each; the first 32 floats used
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
-  __shared__ RowsStage<D> sm;
+  constexpr int NI = kBT * D * 2 / 1024;  // 1 KiB loads per operand tile
+  __shared__ RowsStage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, B = a.num_seqs;
-  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  int pair, y;
+  die_task(pair, y);
+  const int b = pair / Hkv, g = pair % Hkv;
   const int ctx = clamp_ctx(a, b);
-  const int k0 = blockIdx.y * 128;
+  const int k0 = y * 128;
   if (k0 >= ctx) return;
   const int q0 = a.cu_q_lens[b], qlen = a.cu_q_lens[b + 1] - q0;
   const int nrows = qlen * G, pos_base = ctx - qlen;
@@ -246,52 +270,79 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
+  // per-lane source offsets of this wave's loads (the same for every tile)
+  uint32_t voff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int m = i * 64 + lane;  // 16-byte slot of the operand tile
+    if (wave < 2) {               // row tile: slot m holds chunk pos of row r
+      const int r = m / CPR, pos = m % CPR, j = pos ^ (r % CPR);
+      voff[i] = static_cast<uint32_t>(((r / G) * Hq + (r % G)) * D * 2 + j * 16);
+    } else {                      // col tile: half c, feature d, 8-row chunk
+      const int c = m / (D * 2), w2 = m % (D * 2), d = w2 / 2, e = (w2 % 2) ^ ((d >> 3) & 1);
+      voff[i] = static_cast<uint32_t>((d * a.lpad + 16 * c + 8 * e) * 2);
+    }
+  }
+  const int64_t rowbase = (static_cast<int64_t>(g) * B + b) * a.lpad;
+  const int64_t colbase = (static_cast<int64_t>(g) * B + b) * D * a.lpad;
+  const int32_t col_bytes = ((D - 1) * a.lpad + kBT) * 2;
+  auto stage_tile = [&](int it, int s) {
+    const int R0 = it * kBT;
+    RowsStage<D>& st = sm[s];
+    const void* src;
+    int32_t nb;
+    uint32_t lds;
+    if (wave < 2) {
+      const int t0 = R0 / G;
+      src = (wave == 0 ? a.q : a.dout) + (static_cast<int64_t>(q0 + t0) * Hq + g * G) * D;
+      nb = max(0, min(qlen - t0, kBT / G)) * Hq * D * 2;  // the tile's tokens; past the sequence: 0
+      lds = lds_address(wave == 0 ? st.q : st.d);
+    } else {
+      src = (wave == 2 ? a.qt : a.dot) + colbase + R0;
+      nb = col_bytes;
+      lds = lds_address(wave == 2 ? st.qt : st.dt);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(src, nb, voff[i], lds + i * 1024);
+    if (wave < 2)
+      dma16((wave == 0 ? a.lse2 : a.delta) + rowbase + R0, kBT * 4, lane * 16,
+            lds_address(wave == 0 ? st.lse2 : st.delta));
+  };
+
   // query tiles that see a key of this workgroup (causal: from the token at
-  // position k0 on)
+  // position k0 on), walked from the last one down: the workgroups of one
+  // pair then read the same tiles at about the same time
   const int t_first = a.causal ? max(0, k0 - pos_base) : 0;
   const int tile0 = (t_first * G) / kBT, n_tiles = (nrows + kBT - 1) / kBT;
-  const int64_t rowbase = (static_cast<int64_t>(g) * B + b) * a.lpad;
-  for (int it = tile0; it < n_tiles; ++it) {
+  if (tile0 < n_tiles) stage_tile(n_tiles - 1, 0);
+  wait_vmcnt<0>();
+  // a query row R (token R / G) sees this lane's key when R >= lo_row
+  const int lo_row = a.causal ? (key - pos_base) * G : INT_MIN;
+  const bool key_ok = key < ctx;
+  for (int it = n_tiles - 1; it >= tile0; --it) {
     const int R0 = it * kBT;
-    __syncthreads();  // the previous tile's reads are done
-    for (int idx = tid; idx < kBT * CPR; idx += 256) {
-      const int r = idx / CPR, c = idx % CPR, R = R0 + r;
-      u32x4 qv = {0, 0, 0, 0}, dv_ = {0, 0, 0, 0};
-      if (R < nrows) {
-        const int64_t row = static_cast<int64_t>(q0 + R / G) * Hq + (g * G + R % G);
-        qv = *reinterpret_cast<const u32x4*>(a.q + row * D + c * 8);
-        dv_ = *reinterpret_cast<const u32x4*>(a.dout + row * D + c * 8);
-      }
-      *reinterpret_cast<u32x4*>(sm.q + row_pos<D>(r, c)) = qv;
-      *reinterpret_cast<u32x4*>(sm.d + row_pos<D>(r, c)) = dv_;
-    }
-    for (int idx = tid; idx < D * 4; idx += 256) {
-      const int d = idx / 4, c = (idx / 2) % 2, e = idx % 2;
-      const int64_t off = ((static_cast<int64_t>(g) * D + d) * B + b) * a.lpad + R0 + 16 * c + 8 * e;
-      *reinterpret_cast<u32x4*>(sm.qt + col_pos<D>(d, c, e)) = *reinterpret_cast<const u32x4*>(a.qt + off);
-      *reinterpret_cast<u32x4*>(sm.dt + col_pos<D>(d, c, e)) = *reinterpret_cast<const u32x4*>(a.dot + off);
-    }
-    if (tid < kBT) sm.lse2[tid] = a.lse2[rowbase + R0 + tid];
-    else if (tid < 2 * kBT) sm.delta[tid - kBT] = a.delta[rowbase + R0 + tid - kBT];
-    __syncthreads();
+    const int s = (n_tiles - 1 - it) & 1;
+    __syncthreads();  // tile it has landed; the stage of the tile before is free
+    if (it > tile0) stage_tile(it - 1, s ^ 1);
+    const RowsStage<D>& st = sm[s];
 
     // S and dP for (query rows x this lane's key)
-    f32x16 s = {}, dp = {};
+    f32x16 sv = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(sm.q, col, 2 * ks + half), kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(sm.d, col, 2 * ks + half), vf[ks], dp, 0, 0, 0);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.q, col, 2 * ks + half), kf[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.d, col, 2 * ks + half), vf[ks], dp, 0, 0, 0);
     }
     float p[16], ds[16];
 #pragma unroll
     for (int bq = 0; bq < 4; ++bq) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(sm.lse2 + 8 * bq + 4 * half);
-      const f32x4 dl = *reinterpret_cast<const f32x4*>(sm.delta + 8 * bq + 4 * half);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(st.lse2 + 8 * bq + 4 * half);
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(st.delta + 8 * bq + 4 * half);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = 4 * bq + r, R = R0 + 8 * bq + 4 * half + r;
-        const bool vis = R < nrows && key < ctx && (!a.causal || key <= pos_base + R / G);
-        p[v] = vis ? fast_exp2(__builtin_fmaf(s[v], sc, -l2[r])) : 0.f;
+        const bool vis = key_ok & (R < nrows) & (R >= lo_row);
+        p[v] = vis ? fast_exp2(__builtin_fmaf(sv[v], sc, -l2[r])) : 0.f;
         ds[v] = vis ? p[v] * (dp[v] - dl[r]) : 0.f;
       }
     }
@@ -302,10 +353,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int d = db * 32 + col;
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(sm.dt, d, c, half), pb, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(sm.qt, d, c, half), sb, dk[db], 0, 0, 0);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(st.dt, d, c, half), pb, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(st.qt, d, c, half), sb, dk[db], 0, 0, 0);
       }
     }
+    wait_vmcnt<0>();  // this wave's loads of the next tile are in LDS
   }
 
   // write this lane's key: dK token-major, dV feature-major (the pool's layouts)
@@ -328,8 +380,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (sequence, KV head, 128 query rows), wave w owning
 // rows 32w..32w+31 with its Q and dO rows as MFMA operands; the key tiles
-// (32 keys, two pages) it sees are staged in LDS: K and V token-major, K
-// feature-major.
+// (32 keys, two pages) it sees are staged in LDS, two stages deep: K and V
+// token-major, K feature-major -- six page groups, each wave moving one
+// instruction's worth of every group.
 template <int D>
 struct KeysStage {
   uint16_t k[kBT * D], v[kBT * D], kt[kBT * D];
@@ -338,15 +391,18 @@ struct KeysStage {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
-  __shared__ KeysStage<D> sm;
+  constexpr int PER = kPage * D * 2 / 1024;  // 1 KiB loads per page group
+  __shared__ KeysStage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv, B = a.num_seqs;
-  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  int pair, y;
+  die_task(pair, y);
+  const int b = pair / Hkv, g = pair % Hkv;
   const int q0 = a.cu_q_lens[b], qlen = a.cu_q_lens[b + 1] - q0;
   const int nrows = qlen * G;
-  const int W0 = blockIdx.y * 128;
+  const int W0 = y * 128;
   if (W0 >= nrows) return;
   const int ctx = clamp_ctx(a, b);
   const int pos_base = ctx - qlen;
@@ -374,47 +430,73 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
+  // this wave's instruction of each of the six page groups: K page 0/1 and V
+  // page 0/1 (row layout), K^T page 0/1 (col layout); PER instructions per
+  // group, instruction u = i*4 + wave
+  constexpr int NI = 6 * PER / 4;
+  uint32_t voff[NI], ldso[NI];
+  int grp[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int u = i * 4 + wave, gr = u / PER, sub = u % PER;
+    const int m = sub * 64 + lane, p = gr & 1;
+    grp[i] = gr;
+    if (gr < 4) {
+      const int r1 = m / CPR, pos = m % CPR, r = 16 * p + r1, j = pos ^ (r % CPR);
+      voff[i] = static_cast<uint32_t>(r1 * D * 2 + j * 16);
+      ldso[i] = static_cast<uint32_t>((16 * p * CPR + m) * 16);
+    } else {
+      const int d = m / 2, e = (m % 2) ^ ((d >> 3) & 1);
+      voff[i] = static_cast<uint32_t>((d * kPage + 8 * e) * 2);
+      ldso[i] = static_cast<uint32_t>(p * D * 32 + m * 16);
+    }
+  }
+  auto stage_tile = [&](int kt, int s) {
+    int64_t chunk[2];
+    int32_t nb[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int32_t ph = page_id(a, b, 2 * kt + p, n_pages);
+      chunk[p] = (static_cast<int64_t>(ph < 0 ? 0 : ph) * Hkv + g) * (kPage * D);
+      nb[p] = ph < 0 ? 0 : kPage * D * 2;
+    }
+    const uint32_t base_k = lds_address(sm[s].k), base_v = lds_address(sm[s].v),
+                   base_t = lds_address(sm[s].kt);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int gr = grp[i], p = gr & 1;
+      const uint16_t* src = gr < 2 ? a.k : (gr < 4 ? a.vtm : a.kfm);
+      const uint32_t lb = gr < 2 ? base_k : (gr < 4 ? base_v : base_t);
+      dma16(src + chunk[p], nb[p], voff[i], lb + ldso[i]);
+    }
+  };
+
   const int t_last = min(W0 + 127, nrows - 1) / G;
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   const int n_kt = (kmax + kBT - 1) / kBT;
+  if (n_kt > 0) stage_tile(0, 0);
+  wait_vmcnt<0>();
+  // the last key this lane's row sees (none when the row is past the sequence)
+  const int key_lim = row_ok ? (a.causal ? min(qpos, ctx - 1) : ctx - 1) : -1;
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    for (int idx = tid; idx < kBT * CPR; idx += 256) {  // K, V rows of keys 32kt + r
-      const int r = idx / CPR, c = idx % CPR;
-      const int32_t phys = page_id(a, b, 2 * kt + r / kPage, n_pages);
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (phys >= 0) {
-        const int64_t off = (static_cast<int64_t>(phys) * Hkv + g) * (kPage * D) + (r % kPage) * D + c * 8;
-        kv = *reinterpret_cast<const u32x4*>(a.k + off);
-        vv = *reinterpret_cast<const u32x4*>(a.vtm + off);
-      }
-      *reinterpret_cast<u32x4*>(sm.k + row_pos<D>(r, c)) = kv;
-      *reinterpret_cast<u32x4*>(sm.v + row_pos<D>(r, c)) = vv;
-    }
-    for (int idx = tid; idx < D * 4; idx += 256) {  // K^T of page c of the tile
-      const int d = idx / 4, c = (idx / 2) % 2, e = idx % 2;
-      const int32_t phys = page_id(a, b, 2 * kt + c, n_pages);
-      u32x4 w = {0, 0, 0, 0};
-      if (phys >= 0)
-        w = *reinterpret_cast<const u32x4*>(a.kfm + (static_cast<int64_t>(phys) * Hkv + g) * (kPage * D) +
-                                            d * kPage + e * 8);
-      *reinterpret_cast<u32x4*>(sm.kt + col_pos<D>(d, c, e)) = w;
-    }
-    __syncthreads();
+    const int s = kt & 1;
+    __syncthreads();  // tile kt has landed; the stage of tile kt-1 is free
+    if (kt + 1 < n_kt) stage_tile(kt + 1, s ^ 1);
+    const KeysStage<D>& st = sm[s];
 
     // S^T and dP^T for (keys x this lane's row)
-    f32x16 s = {}, dp = {};
+    f32x16 sv = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(sm.k, col, 2 * ks + half), qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(sm.v, col, 2 * ks + half), dof[ks], dp, 0, 0, 0);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.k, col, 2 * ks + half), qf[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.v, col, 2 * ks + half), dof[ks], dp, 0, 0, 0);
     }
     float ds[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = kt * kBT + 8 * (v >> 2) + 4 * half + (v & 3);
-      const bool vis = row_ok && key < ctx && (!a.causal || key <= qpos);
-      const float p = vis ? fast_exp2(__builtin_fmaf(s[v], sc, -l2)) : 0.f;
+      const bool vis = key <= key_lim;
+      const float p = vis ? fast_exp2(__builtin_fmaf(sv[v], sc, -l2)) : 0.f;
       ds[v] = vis ? p * (dp[v] - dl) : 0.f;
     }
     // dQ^T += K^T dS^T  (contract the 32 keys)
@@ -423,9 +505,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       const bf16x8 sb = rows_to_b(ds, c);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(sm.kt, db * 32 + col, c, half), sb,
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(st.kt, db * 32 + col, c, half), sb,
                                                           acc[db], 0, 0, 0);
     }
+    wait_vmcnt<0>();  // tile kt+1 is in LDS
   }
   if (!row_ok) return;
 #pragma unroll

@@ -138,6 +138,42 @@ struct AttnArgs {
   int32_t key_begin;
 };
 
+// One buffer load of 16 bytes per lane straight into LDS: lane i's bytes
+// [voffset, voffset + 16) of the buffer [base, base + nbytes) land at
+// lds_addr + 16 * i; bytes at or past nbytes read as zero.  Written as inline
+// asm so the compiler's wait-count pass does not drain all outstanding loads
+// before each write of M0 (the hardware latches M0 when the load issues);
+// callers wait with wait_vmcnt<>() before the data is used.  The instruction
+// writes no register.  The compiler's hazard pass does not look inside inline
+// asm, so the asm carries its own wait states: s_nop 4 (five) covers both a
+// VALU write of a descriptor SGPR (v_readfirstlane) before a vector-memory
+// read of it (five wait states) and an M0 write before an LDS DMA (one).
+__device__ __forceinline__ void dma16(const void* base, int32_t nbytes, uint32_t voffset,
+                                      uint32_t lds_addr) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))),
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffff)),
+                    __builtin_amdgcn_readfirstlane(nbytes), kRsrcWord3};
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rs), "{m0}"(m0)
+               : "memory");
+}
+
+// The LDS address (offset in the workgroup's LDS) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// Wait until at most n of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Full-wave max and sum (64 lanes).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -272,8 +308,8 @@ struct BwdArgs {
   float scale;
   int32_t causal;
   int32_t lpad;             // query rows per (KV head, sequence) in the row workspaces
-  uint16_t* qt;             // Q^T  [Hkv][D][B][lpad]
-  uint16_t* dot;            // dO^T [Hkv][D][B][lpad]
+  uint16_t* qt;             // Q^T  [Hkv][B][D][lpad]
+  uint16_t* dot;            // dO^T [Hkv][B][D][lpad]
   float* delta;             // rowsum(dO * O) [Hkv][B][lpad]
   float* lse2;              // lse * log2(e)  [Hkv][B][lpad]
   uint16_t* kfm;            // K pages feature-major [NB, Hkv, D, 16]
