@@ -413,6 +413,9 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="MB of scratch written between steps to evict the 256 MB last-level "
                          "cache (-1 = 512 when a decode call reads less than 512 MB of KV)")
+    ap.add_argument("--fp8-products", action="store_true",
+                    help="prefill calls on fp8 pools use pa_prefill_fp8 (Q and P in E4M3, "
+                         "both products on the fp8 matrix cores)")
     ap.add_argument("--one-call", action="store_true",
                     help="also time a shared-prefix workload's calls joined into one call "
                          "(pa_prefill and pa_prefill_shared_prefix), outside the step")
@@ -477,10 +480,12 @@ def main():
                 S = pa.prefill_num_splits(B, wl.num_kv_heads, Hq, mq, mc)
                 ws = torch.empty(max(1, pa.prefill_workspace_bytes(B, mq, Hq, D, S)),
                                  dtype=torch.uint8, device=dev)
+                f8 = args.fp8_products and wl.kv_dtype == "fp8"
                 fn = (lambda pool=pool, q=q, cu=cu, ctx=ctx, bt=bt, mq=mq, mc=mc, o=o, lse=lse, wl=wl,
-                      c=call, S=S, ws=ws:
+                      c=call, S=S, ws=ws, f8=f8:
                       pa.prefill(pool, q, cu, ctx, bt, wl.scale, causal=c.causal, max_q_len=mq,
-                                 max_ctx_len=mc, out=o, lse=lse, num_splits=S, workspace=ws))
+                                 max_ctx_len=mc, out=o, lse=lse, num_splits=S, workspace=ws,
+                                 fp8_products=f8))
             else:
                 B, Hq, D = q.shape
                 S = args.decode_splits or pa.decode_choose_splits(

@@ -200,6 +200,28 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
                      float scale, int32_t causal, int32_t num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ fp8 products
+ * pa_prefill for an fp8 pool with both products on the fp8 matrix cores
+ * (FlashAttention-3's low-precision forward: the survey page, FlashAttention-3
+ * section), the cache's per-page scales kept exact:
+ *   - each query row is quantised to E4M3 with its own scale amax/448;
+ *   - S = (Q codes . K codes) * q scale * K page scale, in fp32;
+ *   - the online softmax runs in fp32 as in pa_prefill; each weight P (<= 2^8)
+ *     is multiplied by its key's V page scale over the largest V page scale
+ *     of the workgroup's keys and by 448/256, rounded to E4M3, and
+ *     multiplied with the V codes; the row sum uses the unrounded weights.
+ * So Q and P each carry E4M3 rounding (relative 2^-4) on top of the pool's;
+ * results stay within the fp8-KV bound of 6e-2 on the library's tests.
+ * Arguments, layouts, key splits, workspace and errors as pa_prefill, except:
+ * the pool must be PA_FP8_E4M3 (else PA_ERR_UNSUPPORTED), q bf16.
+ */
+pa_status pa_prefill_fp8(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                         float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                         const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                         float scale, int32_t causal, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------ backward
  * Gradients of pa_prefill's attention for an upstream gradient dout, from the
  * forward's output o and logsumexp lse: the attention weights are recomputed

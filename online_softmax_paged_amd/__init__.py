@@ -54,6 +54,9 @@ _gather = _sig("pa_gather_kv", ctypes.c_int, [_P, _VP, _I32, _VP, _VP, _I32, _I3
 _prefill = _sig("pa_prefill", ctypes.c_int,
                 [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                  _F, _I32, _I32, _VP, _SZ, _VP])
+_prefill_fp8 = _sig("pa_prefill_fp8", ctypes.c_int,
+                    [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                     _F, _I32, _I32, _VP, _SZ, _VP])
 _pre_splits = _sig("pa_prefill_num_splits", _I32, [_I32, _I32, _I32, _I32, _I32])
 _pre_ws = _sig("pa_prefill_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32, _I32])
 _sp_splits = _sig("pa_shared_prefix_num_splits", ctypes.c_int,
@@ -93,7 +96,7 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_prefill_workspace_bytes", "pa_shared_prefix_num_splits",
             "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
             "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits",
-            "pa_backward_workspace_bytes", "pa_prefill_backward"]
+            "pa_backward_workspace_bytes", "pa_prefill_backward", "pa_prefill_fp8"]
 
 DECODE_BALANCED = -1
 
@@ -252,9 +255,11 @@ def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, sca
             causal: bool = True, max_q_len: int | None = None, max_ctx_len: int | None = None,
             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
             num_splits: int = 0, workspace: torch.Tensor | None = None,
-            validate: bool = False, stream=None):
+            validate: bool = False, stream=None, fp8_products: bool = False):
     """Attention of query chunks (the last q_len_b positions of each sequence).
-    Returns (o, lse): o like q, lse float32 [T, Hq]."""
+    Returns (o, lse): o like q, lse float32 [T, Hq].  fp8_products (fp8 pools
+    only): Q and P quantised to E4M3 and both products on the fp8 matrix
+    cores (pa_prefill_fp8)."""
     B = int(ctx_lens.numel())
     if max_q_len is None or max_ctx_len is None or validate:
         cu = cu_q_lens.cpu()
@@ -276,11 +281,12 @@ def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, sca
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    _check(_prefill(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(cu_q_lens),
-                    _ptr(ctx_lens), _ptr(block_table), block_table.shape[1], B, Hq, max_q_len,
-                    max_ctx_len, scale, 1 if causal else 0, num_splits,
-                    _ptr(workspace) if need else None, workspace.numel() if need else 0,
-                    _stream(stream)), "pa_prefill")
+    fn, name = (_prefill_fp8, "pa_prefill_fp8") if fp8_products else (_prefill, "pa_prefill")
+    _check(fn(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(cu_q_lens),
+              _ptr(ctx_lens), _ptr(block_table), block_table.shape[1], B, Hq, max_q_len,
+              max_ctx_len, scale, 1 if causal else 0, num_splits,
+              _ptr(workspace) if need else None, workspace.numel() if need else 0,
+              _stream(stream)), name)
     return o, lse
 
 

@@ -91,7 +91,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 5; }
+int32_t pa_abi_version(void) { return 6; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
@@ -198,12 +198,12 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t n
   return o_bytes + rows * sizeof(float);
 }
 
-pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
-                     float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
-                     const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
-                     int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
-                     float scale, int32_t causal, int32_t num_splits, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+static pa_status prefill_impl(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                              float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                              const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                              float scale, int32_t causal, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream, bool fp8_mma) {
   if (num_seqs == 0 && pool) return check_pool(pool);
   pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
                            num_q_heads, max_ctx_len, scale);
@@ -214,8 +214,10 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
     num_splits = pa_prefill_num_splits(num_seqs, pool->num_kv_heads, num_q_heads, max_q_len,
                                        max_ctx_len);
   if (pool->kv_dtype == PA_F32) num_splits = 1;  // the fp32 kernel does not split keys
+  if (fp8_mma && pool->kv_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
                          num_q_heads, max_ctx_len, scale);
+  a.fp8_mma = fp8_mma ? 1 : 0;
   a.cu_q_lens = cu_q_lens;
   a.max_q_len = max_q_len;
   a.causal = causal ? 1 : 0;
@@ -232,6 +234,28 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
     a.part_rows = static_cast<int64_t>(num_seqs) * max_q_len;
   }
   return launched(launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                     float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                     const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                     float scale, int32_t causal, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return prefill_impl(pool, q, q_dtype, o, lse, cu_q_lens, ctx_lens, block_table, bt_stride,
+                      num_seqs, num_q_heads, max_q_len, max_ctx_len, scale, causal, num_splits,
+                      workspace, workspace_bytes, stream, false);
+}
+
+pa_status pa_prefill_fp8(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                         float* lse, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                         const int32_t* block_table, int32_t bt_stride, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                         float scale, int32_t causal, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return prefill_impl(pool, q, q_dtype, o, lse, cu_q_lens, ctx_lens, block_table, bt_stride,
+                      num_seqs, num_q_heads, max_q_len, max_ctx_len, scale, causal, num_splits,
+                      workspace, workspace_bytes, stream, true);
 }
 
 pa_status pa_shared_prefix_num_splits(int32_t num_seqs, int32_t num_kv_heads,

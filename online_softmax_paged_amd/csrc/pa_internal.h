@@ -136,6 +136,9 @@ struct AttnArgs {
   int32_t packed_q;
   // Keys below this position (a multiple of 16) are left out.
   int32_t key_begin;
+  // Prefill of an fp8 pool with Q and P quantised to E4M3 and both products
+  // on the fp8 MFMA (no packed_q or key_begin).
+  int32_t fp8_mma;
 };
 
 // One buffer load of 16 bytes per lane straight into LDS: lane i's bytes

@@ -805,6 +805,366 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
   if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// fp8 pools with every product on the fp8 MFMA (v_mfma_scale_f32_32x32x64_
+// f8f6f4, E4M3 operands): FlashAttention-3's FP8 forward (the survey page,
+// FlashAttention-3 section: low precision with block quantisation) fitted to
+// the paged cache's per-page scales.
+//   Q: each query row x is split in two E4M3 parts with one row scale
+//      sq = amax/448: hi = E4M3(x/sq) and lo = E4M3((x/sq - hi) * 16); the
+//      lo product enters the same accumulator through the instruction's block
+//      scale 2^-4, so S carries Q to about 2^-8 relative (one E4M3 part alone
+//      moves S by up to 2^-4 relative, which shifts the weights of rows that
+//      see few keys).  K: the pool's codes; S = Q.Kc * sk(page).
+//   P: the online softmax's weights (<= 1: the running max is updated exactly)
+//      times their key's V page scale over the largest V page scale of the
+//      workgroup's keys, times 448, rounded to E4M3; O accumulates Pc . Vc and
+//      is multiplied back by sv_max / 448 at the end.  O is divided by the sum
+//      of the rounded weights it was built from, so it is the weighted mean of
+//      V under weights each within 2^-4 relative of the exact ones (normal
+//      E4M3 codes); the logsumexp uses the sum of the unrounded weights.
+// Tiles of 64 keys (four pages; one 64-deep k-step for P.V).  K and V codes
+// move by buffer loads straight into LDS, three stages of 16 KiB (d = 128):
+//   K [64 keys][D/16 chunks of 16 B], chunk c of key i at c ^ (i % (D/16));
+//   V per page [D][16 keys], as in the pool.
+// An operand lane of group g (lane / 32) holds k = 32g .. 32g+31 of each
+// 64-deep k-step in A and B alike (any common order contracts the same).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct Fp8Smem {
+  static constexpr int KB = 64 * D;          // K codes of a tile
+  static constexpr int VB = 4 * kPage * D;   // V codes of a tile
+  static constexpr int STAGE = KB + VB;
+  char buf[3 * STAGE];
+};
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// the same with B's block scale 2^-4 (E8M0 123)
+__device__ __forceinline__ f32x16 mfma_fp8_b16th(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 123);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
+  __shared__ Fp8Smem<D> sm;
+  constexpr int KT = 64;             // keys per tile
+  constexpr int CK = D / 16;         // 16-byte chunks per K row
+  constexpr int NI = D / 32;         // buffer loads per wave per tile (16 KiB / 1 KiB / 4)
+  constexpr int STAGE = Fp8Smem<D>::STAGE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  // die-aware task order, as in the bf16 kernel
+  const int S = a.num_splits;
+  const int n_bg = gridDim.x, n_y = gridDim.y;
+  const int lin = blockIdx.y * n_bg + blockIdx.x;
+  int bg = blockIdx.x, y = blockIdx.y;
+  if (n_bg % 8 == 0) {
+    const int P = n_bg / 8, GP = (P % 2 == 0) ? 2 : 1;
+    const int j = lin / 8, per_group = GP * n_y;
+    const int grp = j / per_group, i = j % per_group;
+    bg = (lin % 8) * P + grp * GP + i % GP;
+    y = i / GP;
+  }
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tile = n_tiles - 1 - y / S, split = y % S;
+  const int TQ = 128 / G;
+
+  const int q0 = a.cu_q_lens[b];
+  const int qlen = a.cu_q_lens[b + 1] - q0;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
+  const int t0 = tile * TQ;
+  if (t0 >= qlen) return;
+  const int pos_base = ctx - qlen;
+  const int t_last = min(t0 + TQ, qlen) - 1;
+  const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
+  if (kmax <= 0) return;
+  const int n_kt_all = (kmax + KT - 1) / KT;
+  const int per_split = (n_kt_all + S - 1) / S;
+  const int kt_begin = split * per_split;
+  const int n_kt = min(n_kt_all, kt_begin + per_split);
+  const int n_pages = (ctx + kPage - 1) / kPage;
+  const int first_pos = pos_base + t0;
+  const int n_full = a.causal ? max(0, min((first_pos + 1) / KT, ctx / KT)) : ctx / KT;
+  const int tail_tile = (ctx % kPage) ? (ctx - 1) / KT : -1;
+
+  const int r = wave * 32 + col;
+  const int tt = t0 + r / G, hg = r % G;
+  const bool row_ok = tt < qlen;
+  const int qpos = pos_base + tt;
+  const int key_lim = a.causal ? min(qpos, ctx - 1) : ctx - 1;
+  const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+
+  // largest V page scale among this workgroup's keys (the P.V reference)
+  float sv_max = 0.f;
+  {
+    const int p1 = min(n_pages, n_kt * (KT / kPage));
+    for (int p = kt_begin * (KT / kPage) + lane; p < p1; p += 64) {
+      const int32_t id = bt[p];
+      if (id >= 0 && id < a.num_blocks) sv_max = fmaxf(sv_max, a.v_scale[id]);
+    }
+    sv_max = wave_max(sv_max);
+    if (!(sv_max > 0.f)) sv_max = 1.f;
+  }
+  const float p_scale = 448.f / sv_max;
+
+  // page ids: 64 at a time in a lane vector (16 tiles)
+  int id_chunk = -1;
+  int32_t idv = -1;
+  auto page_at = [&](int t, int j) -> int32_t {
+    const int p = 4 * t + j;
+    const int c = p >> 6;
+    if (c != id_chunk) {
+      id_chunk = c;
+      idv = 64 * c + lane < n_pages ? bt[64 * c + lane] : -1;
+      asm volatile("" ::"v"(idv));
+    }
+    const int32_t id = __builtin_amdgcn_readlane(idv, p & 63);
+    return p < n_pages && id >= 0 && id < a.num_blocks ? id : -1;
+  };
+  // this wave's loads of a tile: u = i*4 + wave; K loads first (D/16 of them),
+  // then V; each covers 64 lanes x 16 B of one page
+  uint32_t voff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int u = i * 4 + wave;
+    if (u < D / 16) {
+      const int m = u * 64 + lane, key = m / CK, pos = m % CK, c = pos ^ (key % CK);
+      voff[i] = static_cast<uint32_t>((key % kPage) * D + c * 16);
+    } else {
+      voff[i] = static_cast<uint32_t>(((u - D / 16) * 64 + lane) % D * 16);
+    }
+  }
+  const uint32_t lds0 = lds_address(sm.buf);
+  auto dma_tile = [&](int t, uint32_t stage) {
+    int32_t ph[4];
+    int nv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ph[j] = page_at(t, j);
+      nv[j] = min(kPage, max(0, ctx - (4 * t + j) * kPage));
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int u = i * 4 + wave;
+      const bool is_v = u >= D / 16;
+      const int pj = is_v ? (u - D / 16) * 64 / D : (u * 64 / CK) / kPage;
+      const int32_t id = ph[pj];
+      const int64_t chunk = (static_cast<int64_t>(id < 0 ? 0 : id) * Hkv + g) * (kPage * D);
+      const int32_t nb = id < 0 ? 0 : (is_v ? (nv[pj] > 0 ? kPage * D : 0) : nv[pj] * D);
+      const char* base = static_cast<const char*>(is_v ? a.v : a.k) + chunk;
+      dma16(base, nb, voff[i], stage + u * 1024);
+    }
+  };
+  if (kt_begin < n_kt) {
+    dma_tile(kt_begin, lds0);
+    dma_tile(kt_begin + 1, lds0 + STAGE);
+  }
+
+  // Q row split in two E4M3 parts: this lane holds features 64ks + 32*half .. +31
+  i32x8 qc[D / 64], ql[D / 64];
+  float sq;
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
+    u32x4 raw[D / 64][4];
+    float amax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        raw[ks][c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 64 * ks + 32 * half + 8 * c)
+                            : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[ks][c][k] << 16)),
+                                   fabsf(__builtin_bit_cast(float, raw[ks][c][k] & 0xffff0000u))));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    sq = amax > 0.f ? amax / 448.f : 1.f;
+    const float inv = amax > 0.f ? 448.f / amax : 1.f;
+    auto cl = [](float x) { return fminf(fmaxf(x, -448.f), 448.f); };
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t w0 = raw[ks][c][2 * k], w1 = raw[ks][c][2 * k + 1];
+          const float x0 = cl(__builtin_bit_cast(float, w0 << 16) * inv);
+          const float x1 = cl(__builtin_bit_cast(float, w0 & 0xffff0000u) * inv);
+          const float x2 = cl(__builtin_bit_cast(float, w1 << 16) * inv);
+          const float x3 = cl(__builtin_bit_cast(float, w1 & 0xffff0000u) * inv);
+          const uint32_t h = fp8x4(x0, x1, x2, x3);
+          const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(h), false);
+          const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(h), true);
+          qc[ks][2 * c + k] = static_cast<int>(h);
+          ql[ks][2 * c + k] = static_cast<int>(fp8x4((x0 - d01[0]) * 16.f, (x1 - d01[1]) * 16.f,
+                                                     (x2 - d23[0]) * 16.f, (x3 - d23[1]) * 16.f));
+        }
+  }
+  const float sc = a.scale * kLog2e * sq;
+  float m = -INFINITY, l = 0.f, lq = 0.f, mu = 0.f;  // lq: sum of the rounded weights
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  wait_vmcnt<NI>();  // tile kt_begin landed (kt_begin + 1 may still fly)
+  __syncthreads();
+
+  int st_cur = 0, st_pre = 2;
+  for (int kt = kt_begin; kt < n_kt; ++kt) {
+    char* stg = sm.buf + st_cur * STAGE;
+    if (kt == tail_tile) {
+      // zero V codes of slots at or past the context end (they may be NaN codes)
+      uint32_t* vw = reinterpret_cast<uint32_t*>(stg + Fp8Smem<D>::KB);
+      for (int e = tid; e < 4 * D * 4; e += 256) {
+        const int pg = e / (4 * D), kw = e % 4;
+        const int key0 = kt * KT + pg * kPage + 4 * kw;
+        uint32_t w = vw[e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (key0 + k >= ctx) w &= ~(0xffu << (8 * k));
+        vw[e] = w;
+      }
+      __syncthreads();
+    }
+    if (kt + 2 < n_kt) dma_tile(kt + 2, lds0 + st_pre * STAGE);
+    st_cur = st_cur == 2 ? 0 : st_cur + 1;
+    st_pre = st_pre == 2 ? 0 : st_pre + 1;
+
+    float fac[4], vsc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t id = page_at(kt, j);
+      fac[j] = id < 0 ? 0.f : sc * a.k_scale[id];
+      vsc[j] = id < 0 ? 0.f : p_scale * a.v_scale[id];
+    }
+
+    // S^T = K . Q^T for keys 32*beta .. +31 of the tile
+    f32x16 sacc[2] = {};
+    const int8_t* kb = reinterpret_cast<const int8_t*>(stg);
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta) {
+      const int key = 32 * beta + col;
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks) {
+        const int c0 = 4 * ks + 2 * half;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + (key * CK + (c0 ^ (key % CK))) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + (key * CK + ((c0 + 1) ^ (key % CK))) * 16);
+        i32x8 kaa;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kaa[k] = static_cast<int>(lo[k]);
+          kaa[4 + k] = static_cast<int>(hi[k]);
+        }
+        sacc[beta] = mfma_fp8(kaa, qc[ks], sacc[beta]);
+        sacc[beta] = mfma_fp8_b16th(kaa, ql[ks], sacc[beta]);
+      }
+    }
+    // value v of block beta is key 32*beta + 8*(v/4) + 4*half + v%4, page 2*beta + v/8
+    float sv[32];
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[16 * beta + v] = sacc[beta][v] * fac[2 * beta + (v >> 3)];
+    if (kt >= n_full) {
+      const int lim = key_lim - kt * KT - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
+        sv[i] = off <= lim ? sv[i] : -INFINITY;
+      }
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mt = fmaxf(mt, sv[i]);
+    mt = max_xor32(mt);
+    if (__any(mt > m)) {  // exact running max: every weight <= 1 fills E4M3's range
+      const float m_new = fmaxf(m, mt);
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
+      lq *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      m = m_new;
+      mu = m == -INFINITY ? 0.f : m;
+    }
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      sv[i] = fast_exp2(sv[i] - mu);
+      ps[i & 3] += sv[i];
+    }
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+
+    // P^T codes as the B operand: group g takes keys 32g .. 32g+31
+    i32x8 pb;
+    float pq[4] = {0.f, 0.f, 0.f, 0.f};  // rounded weights (code values) summed per page
+#pragma unroll
+    for (int bq = 0; bq < 4; ++bq) {
+      const float s0 = vsc[bq >> 1], s1 = vsc[2 + (bq >> 1)];
+      const uint32_t d0 = fp8x4(sv[4 * bq] * s0, sv[4 * bq + 1] * s0, sv[4 * bq + 2] * s0, sv[4 * bq + 3] * s0);
+      const uint32_t d1 = fp8x4(sv[16 + 4 * bq] * s1, sv[16 + 4 * bq + 1] * s1, sv[16 + 4 * bq + 2] * s1,
+                                sv[16 + 4 * bq + 3] * s1);
+      const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8(d0, false), c1 = __builtin_amdgcn_cvt_pk_f32_fp8(d0, true);
+      const auto c2 = __builtin_amdgcn_cvt_pk_f32_fp8(d1, false), c3 = __builtin_amdgcn_cvt_pk_f32_fp8(d1, true);
+      pq[bq >> 1] += (c0[0] + c0[1]) + (c1[0] + c1[1]);
+      pq[2 + (bq >> 1)] += (c2[0] + c2[1]) + (c3[0] + c3[1]);
+      const auto e = __builtin_amdgcn_permlane32_swap(d0, d1, false, false);
+      pb[2 * bq] = static_cast<int>(e[0]);
+      pb[2 * bq + 1] = static_cast<int>(e[1]);
+    }
+    // O^T += V^T . P^T: V codes of pages 2g, 2g+1 for feature d
+    const int8_t* vb = reinterpret_cast<const int8_t*>(stg + Fp8Smem<D>::KB);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = db * 32 + col;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (2 * half) * (kPage * D) + d * kPage);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (2 * half + 1) * (kPage * D) + d * kPage);
+      i32x8 va;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        va[k] = static_cast<int>(lo[k]);
+        va[4 + k] = static_cast<int>(hi[k]);
+      }
+      acc[db] = mfma_fp8(va, pb, acc[db]);
+    }
+    // back to weights: code sum of page j over its factor vsc[j] (0 for pages
+    // without keys, whose codes are 0)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lq += vsc[j] > 0.f ? pq[j] / vsc[j] : 0.f;
+    if (kt + 2 < n_kt) wait_vmcnt<NI>(); else wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  wait_vmcnt<0>();
+  l = sum_xor32(l);
+  lq = sum_xor32(lq);
+  if (!row_ok) return;
+  // acc holds codes: times sv_max / 448 it is sum(w V); write_rows divides
+  // by l, so fold l / lq in to divide by the rounded weights' sum instead
+  const float back = sv_max * (1.f / 448.f) * (lq > 0.f ? l / lq : 0.f);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] *= back;
+  write_rows<D>(a, acc, m, l, qrow, split, half);
+}
+
 // Merge of the key splits of every query row: the logsumexp-weighted sum of
 // its S normalised partial rows (one wave per (sequence, token, head); empty
 // splits carry lse = -inf and weight 0).
@@ -883,10 +1243,14 @@ hipError_t launch_pass(const AttnArgs& a, hipStream_t st) {
   const int n_tiles = (n_q + TQ - 1) / TQ;
   const int n_seq = a.packed_q > 0 ? 1 : a.num_seqs;
   const dim3 grid(n_seq * a.num_kv_heads, n_tiles * a.num_splits);
-  if (a.kv_dtype == PA_FP8_E4M3)
+  if (a.fp8_mma) {
+    const int tq = 128 / G, nt = (n_q + tq - 1) / tq;
+    prefill_fp8mma_kernel<D><<<dim3(n_seq * a.num_kv_heads, nt * a.num_splits), 256, 0, st>>>(a, nt);
+  } else if (a.kv_dtype == PA_FP8_E4M3) {
     prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, n_tiles);
-  else
+  } else {
     prefill_dma_kernel<D, NW><<<grid, 64 * NW, 0, st>>>(a, n_tiles);
+  }
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 5
+    assert pa.abi_version() == 6
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -230,6 +230,24 @@ def test_backward_checks():
         assert _backward(p, ws=0x100000, ws_bytes=need, **bad) == pa.PA_ERR_INVALID_ARG, bad
     assert _backward(p, ws=0x100008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG
     assert _backward(p, B=0) == pa.PA_OK
+
+
+def test_prefill_fp8_checks():
+    def call(pool, **kw):
+        a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, cu=0x8000, ctx=0x9000,
+                 bt=0xa000, stride=4, B=2, Hq=8, max_q=64, max_ctx=64, scale=0.1, causal=1,
+                 splits=1, ws=0, ws_bytes=0)
+        a.update(kw)
+        return pa._prefill_fp8(pool.c, a["q"], a["q_dtype"], a["o"], a["lse"], a["cu"], a["ctx"],
+                               a["bt"], a["stride"], a["B"], a["Hq"], a["max_q"], a["max_ctx"],
+                               a["scale"], a["causal"], a["splits"], a["ws"], a["ws_bytes"], None)
+    assert call(_FakePool()) == pa.PA_ERR_UNSUPPORTED                       # bf16 pool
+    assert call(_FakePool(kv_dtype=pa.PA_F32), q_dtype=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
+    f = _FakePool(kv_dtype=pa.PA_FP8_E4M3)
+    assert call(f, q_dtype=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
+    assert call(f, splits=3) == pa.PA_ERR_WORKSPACE
+    assert call(f, max_q=0) == pa.PA_ERR_INVALID_ARG
+    assert call(f, B=0) == pa.PA_OK
 
 
 def test_decode_split_heuristic():

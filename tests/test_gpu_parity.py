@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.pool import gather_kv
 import workloads
 from tests import harness as H
 
@@ -310,6 +311,102 @@ def test_balanced_decode_named_full():
         pool = H.device_pool(wl)
         call = [c for c in wl.calls if c.kind == "decode"][0]
         _check_call(wl, call, pool, opool, num_splits=pa.DECODE_BALANCED)
+
+
+# ------------------------------------------------------------ fp8 products
+FP8MMA_CASES = [
+    # D, Hq, Hkv, ctx_lens, q_lens (None = whole sequences), causal
+    (128, 8, 2, (600, 300, 45, 129), None, True),
+    (128, 8, 2, (600, 300, 900), (128, 1, 77), True),    # chunks and a decode row
+    (128, 8, 2, (300, 70), (100, 70), False),
+    (64, 4, 4, (257, 33), None, True),                   # G = 1
+    (128, 16, 2, (150, 90), (150, 17), True),            # G = 8
+]
+
+
+def _fp8_products_check(opool, wl, call, o, lse, ro, rl):
+    """Bars of the fp8-product path, from E4M3's rounding.
+
+    Each weight w_i reaches P.V as E4M3 code w_i f_i (f_i = 448 times its V
+    page scale over the largest), so the kernel's weights are w_i (1 + e_i) with
+    |e_i| <= 2^-4 for normal codes and |w_i e_i| <= 2^-10 / f_i below them; it
+    divides by their own sum, so per feature d
+        |O'_d - O_d| <= (2^-4 + n 2^-10 / f_min) / (1 - 2^-4) * max_i |v_id - O_d|
+    over the row's n visible keys (the largest weight is 1).  1e-2 is added for
+    the rest: the remainder of Q after its two E4M3 parts, bf16 output
+    rounding, fp32 sums.  The error averages down like 1/sqrt(keys), so rows
+    that see 16 keys or more are held to the fp8-KV bound itself, and every
+    logsumexp (built from the unrounded weights) too.  Returns the max errors
+    of rows seeing >= 16 keys and of the logsumexps."""
+    go = o.detach().to(torch.float64).cpu().numpy()
+    eo_all, el = H.max_err(o, lse, ro, rl)
+    cu = call.cu_q_lens.tolist()
+    G = wl.num_q_heads // wl.num_kv_heads
+    e_long = 0.0
+    for b in range(len(cu) - 1):
+        c = int(call.ctx_lens[b])
+        n = cu[b + 1] - cu[b]
+        if n == 0 or c == 0:
+            continue
+        bt = call.block_table[b].numpy()
+        vs = np.array([opool.v_scale[bt[p]] for p in range((c + 15) // 16)])
+        f_min = 448.0 * vs.min() / vs.max()
+        pos = c - n + np.arange(n)
+        nk = np.minimum(pos + 1, c) if call.causal else np.full(n, c)
+        for g in range(wl.num_kv_heads):
+            _, V = gather_kv(opool, bt, c, g)
+            vmax, vmin = np.maximum.accumulate(V, 0), np.minimum.accumulate(V, 0)
+            for h in range(g * G, (g + 1) * G):
+                O = ro[cu[b]:cu[b + 1], h]
+                spread = np.maximum(vmax[nk - 1] - O, O - vmin[nk - 1])
+                coef = (2.0 ** -4 + nk[:, None] * 2.0 ** -10 / f_min) / (1 - 2.0 ** -4)
+                err = np.abs(go[cu[b]:cu[b + 1], h] - O)
+                assert (err <= coef * spread + 1e-2).all(), (b, h, float((err - coef * spread).max()))
+                if (nk >= 16).any():
+                    e_long = max(e_long, float(err[nk >= 16].max()))
+    return eo_all, e_long, el
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,ctx,ql,causal", FP8MMA_CASES)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_fp8_products_parity(D, Hq, Hkv, ctx, ql, causal, splits):
+    """Q (two E4M3 parts) and P (E4M3) on the fp8 matrix cores, against the
+    oracle under the bars derived from E4M3's rounding; the error of the
+    bf16-product path on the same inputs is logged beside it."""
+    _log(f"fp8 products D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} q={ql} causal={causal} splits={splits}")
+    wl = workloads.small("prefill", kv_dtype="fp8", q_dtype="bf16", num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=D, ctx_lens=ctx, q_lens=ql, seed=140 + D + Hq,
+                         causal=causal)
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    call = wl.calls[0]
+    ro, rl = H.oracle_call(opool, wl, call)
+    o, lse = H.DeviceCall(wl, call).run(pool, num_splits=splits, fp8_products=True)
+    o2, l2 = H.DeviceCall(wl, call).run(pool, num_splits=splits)
+    torch.cuda.synchronize()
+    eo2, el2 = H.max_err(o2, l2, ro, rl)
+    eo, e_long, el = _fp8_products_check(opool, wl, call, o, lse, ro, rl)
+    _log(f"  fp8 products max|dO|={eo:.3e} (rows >= 16 keys {e_long:.3e}) max|dLSE|={el:.3e}; "
+         f"bf16 products {eo2:.3e} {el2:.3e}")
+    assert e_long <= H.TOL["fp8"] and el <= H.TOL["fp8"]
+
+
+def test_prefill_fp8_products_mixed_step_full_size():
+    """The 16-sequence mixed step's chunked prefill (8 x 256 over 1536 fp8
+    keys, every row seeing 1281 keys or more) with fp8 products, every row
+    against the oracle at the fp8-KV bound."""
+    _log("fp8 products: mixed fp8 step, prefill call")
+    wl, opool = _named(5)
+    pool = H.device_pool(wl)
+    call = [c for c in wl.calls if c.kind == "prefill"][0]
+    dc = H.DeviceCall(wl, call)
+    o, lse = dc.run(pool, fp8_products=True)
+    torch.cuda.synchronize()
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    _log(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= H.TOL["fp8"] and el <= H.TOL["fp8"]
+    o2, l2 = dc.run(pool, fp8_products=True)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
 
 
 # ------------------------------------------------------------ shared prefix
