@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 1 MI355X"
 
@@ -413,9 +414,10 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="MB of scratch written between steps to evict the 256 MB last-level "
                          "cache (-1 = 512 when a decode call reads less than 512 MB of KV)")
-    ap.add_argument("--fp8-products", action="store_true",
-                    help="prefill calls on fp8 pools use pa_prefill_fp8 (Q and P in E4M3, "
-                         "both products on the fp8 matrix cores)")
+    ap.add_argument("--bf16-products", action="store_true",
+                    help="prefill calls on fp8 pools use pa_prefill (codes widened to bf16, "
+                         "products on the bf16 matrix cores) instead of pa_prefill_fp8 (Q and "
+                         "P in E4M3, both products on the fp8 matrix cores)")
     ap.add_argument("--one-call", action="store_true",
                     help="also time a shared-prefix workload's calls joined into one call "
                          "(pa_prefill and pa_prefill_shared_prefix), outside the step")
@@ -463,7 +465,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    launches = []   # (kind, wl, fn)
+    launches = []   # (kind, wl, call, fn, fp8 products)
     pools = {}
     for wl in wls:
         pool = pa.KVPool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, device=dev)
@@ -480,13 +482,14 @@ def main():
                 S = pa.prefill_num_splits(B, wl.num_kv_heads, Hq, mq, mc)
                 ws = torch.empty(max(1, pa.prefill_workspace_bytes(B, mq, Hq, D, S)),
                                  dtype=torch.uint8, device=dev)
-                f8 = args.fp8_products and wl.kv_dtype == "fp8"
+                f8 = wl.kv_dtype == "fp8" and not args.bf16_products
                 fn = (lambda pool=pool, q=q, cu=cu, ctx=ctx, bt=bt, mq=mq, mc=mc, o=o, lse=lse, wl=wl,
                       c=call, S=S, ws=ws, f8=f8:
                       pa.prefill(pool, q, cu, ctx, bt, wl.scale, causal=c.causal, max_q_len=mq,
                                  max_ctx_len=mc, out=o, lse=lse, num_splits=S, workspace=ws,
                                  fp8_products=f8))
             else:
+                f8 = False
                 B, Hq, D = q.shape
                 S = args.decode_splits or pa.decode_choose_splits(
                     B, wl.num_kv_heads, mc, int(call.ctx_lens.sum()))
@@ -496,16 +499,16 @@ def main():
                 fn = (lambda pool=pool, q=q, ctx=ctx, bt=bt, mc=mc, o=o, lse=lse, wl=wl, ws=ws, S=S:
                       pa.decode(pool, q, ctx, bt, wl.scale, max_ctx_len=mc, num_splits=S,
                                 workspace=ws, out=o, lse=lse))
-            launches.append((call.kind, wl, call, fn))
+            launches.append((call.kind, wl, call, fn, call.kind == "prefill" and f8))
     flush_mb = args.flush_mb
     if flush_mb < 0:
-        small = any(k == "decode" and decode_kv_bytes(c, w) < 512e6 for k, w, c, _ in launches)
+        small = any(k == "decode" and decode_kv_bytes(c, w) < 512e6 for k, w, c, _, _ in launches)
         flush_mb = 512 if small else 0
     scratch = torch.ones(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        for _, _, _, fn in launches:
+        for _, _, _, fn, _ in launches:
             fn()
     torch.cuda.synchronize()
     if args.copy_calib_mb:
@@ -525,7 +528,7 @@ def main():
             # read (not write) the scratch: evicts the KV from the cache without
             # leaving dirty lines whose write-back would overlap the timed launches
             scratch.sum(dtype=torch.int64)
-        for i, (_, _, _, fn) in enumerate(launches):
+        for i, (_, _, _, fn, _) in enumerate(launches):
             evs[s][i][0].record()
             fn()
             evs[s][i][1].record()
@@ -541,13 +544,14 @@ def main():
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)"}
     parts = {}
-    for (kind, wl, call, _), ms in zip(launches, per_launch_ms):
+    for (kind, wl, call, _, f8), ms in zip(launches, per_launch_ms):
         if kind == "prefill":
             fl = prefill_flops(call, wl.head_dim, wl.num_q_heads)
             tf = fl / (ms * 1e-3) / 1e12
-            peak = PEAK_BF16_TFLOPS
             parts.setdefault("prefill", []).append(
-                {"workload": wl.name, "ms": ms, "tflops": tf, "frac_bf16_peak": tf / peak,
+                {"workload": wl.name, "ms": ms, "tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+                 "products": "fp8" if f8 else "bf16",
+                 "frac_products_peak": tf / (PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS),
                  "flops": fl, "dtype": wl.kv_dtype})
         else:
             by = decode_kv_bytes(call, wl)
@@ -567,13 +571,18 @@ def main():
         ms = sum(d["ms"] for d in dec)
         result["value"] = by / (ms * 1e-3) / 1e9
         result["unit"] = "GB/s"
+    # the arithmetic type of the products: fp8 pools take E4M3 products unless
+    # --bf16-products; their decode widens the codes and runs in fp32/bf16
+    f8_pre = any(p["products"] == "fp8" for p in parts.get("prefill", []))
     result["dtype"] = "bf16" if all(w.kv_dtype == "bf16" for w in wls) else \
-        "+".join(sorted({("bf16-q/fp8-kv" if w.kv_dtype == "fp8" else w.kv_dtype) for w in wls}))
+        ("fp8" if f8_pre else "+".join(sorted({("bf16-q/fp8-kv" if w.kv_dtype == "fp8" else w.kv_dtype)
+                                               for w in wls})))
     result["config"] = {"workload": " + ".join(w.name for w in wls), "cache_flush_mb": flush_mb}
     if pre:
         p = pre[0]
-        result["roofline"] = {"bound": "mfma", "achieved": p["tflops"], "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": p["tflops"] / PEAK_BF16_TFLOPS,
+        pk = PEAK_FP8_TFLOPS if p["products"] == "fp8" else PEAK_BF16_TFLOPS
+        result["roofline"] = {"bound": "mfma", "achieved": p["tflops"], "peak": pk,
+                              "unit": "TFLOP/s", "frac": p["tflops"] / pk,
                               "traffic": traffic_for("prefill.hip", p["workload"])}
     if dec:
         d = dec[0]

@@ -816,13 +816,17 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
 //      scale 2^-4, so S carries Q to about 2^-8 relative (one E4M3 part alone
 //      moves S by up to 2^-4 relative, which shifts the weights of rows that
 //      see few keys).  K: the pool's codes; S = Q.Kc * sk(page).
-//   P: the online softmax's weights (<= 1: the running max is updated exactly)
-//      times their key's V page scale over the largest V page scale of the
-//      workgroup's keys, times 448, rounded to E4M3; O accumulates Pc . Vc and
-//      is multiplied back by sv_max / 448 at the end.  O is divided by the sum
-//      of the rounded weights it was built from, so it is the weighted mean of
-//      V under weights each within 2^-4 relative of the exact ones (normal
-//      E4M3 codes); the logsumexp uses the sum of the unrounded weights.
+//   P: the online softmax's weights (<= 4: the running max moves once a tile's
+//      max passes it by 2 in log2 units) times their key's V page scale over
+//      the largest V page scale of the workgroup's keys, times 112, rounded to
+//      E4M3; the factor enters as log2 in the exponent, next to the K page
+//      scale, so one FMA and one exp2 give each code's input.  O accumulates
+//      Pc . Vc and is multiplied back by sv_max / 112 at the end.  O is divided
+//      by the sum of the rounded weights it was built from (per page, from one
+//      more MFMA of a page-selector operand with the P codes), so it is the
+//      weighted mean of V under weights each within 2^-4 relative of the exact
+//      ones (normal E4M3 codes); the logsumexp uses the sum of the unrounded
+//      weights.
 // Tiles of 64 keys (four pages; one 64-deep k-step for P.V).  K and V codes
 // move by buffer loads straight into LDS, three stages of 16 KiB (d = 128):
 //   K [64 keys][D/16 chunks of 16 B], chunk c of key i at c ^ (i % (D/16));
@@ -920,21 +924,39 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     sv_max = wave_max(sv_max);
     if (!(sv_max > 0.f)) sv_max = 1.f;
   }
-  const float p_scale = 448.f / sv_max;
 
-  // page ids: 64 at a time in a lane vector (16 tiles)
-  int id_chunk = -1;
-  int32_t idv = -1;
-  auto page_at = [&](int t, int j) -> int32_t {
+  // Lane vectors of 64 pages (16 tiles), read out per tile with readlane: the
+  // DMA side keeps the page ids two tiles ahead; the compute side keeps its
+  // own ids, K scales, and log2 and inverse of the P code factors.
+  const float p_scale = 112.f / sv_max;  // weights <= 4 reach codes <= 448
+  auto page_id = [&](int p) -> int32_t {
+    const int32_t id = p < n_pages ? bt[p] : -1;
+    return id >= 0 && id < a.num_blocks ? id : -1;
+  };
+  int d_chunk = -1;
+  int32_t d_idv = -1;
+  auto page_at = [&](int t, int j) -> int32_t {  // DMA side
     const int p = 4 * t + j;
-    const int c = p >> 6;
-    if (c != id_chunk) {
-      id_chunk = c;
-      idv = 64 * c + lane < n_pages ? bt[64 * c + lane] : -1;
-      asm volatile("" ::"v"(idv));
+    if ((p >> 6) != d_chunk) {
+      d_chunk = p >> 6;
+      d_idv = page_id(64 * d_chunk + lane);
+      asm volatile("" ::"v"(d_idv));
     }
-    const int32_t id = __builtin_amdgcn_readlane(idv, p & 63);
-    return p < n_pages && id >= 0 && id < a.num_blocks ? id : -1;
+    return __builtin_amdgcn_readlane(d_idv, p & 63);
+  };
+  int c_chunk = -1;
+  int32_t idv = -1;
+  float ksv = 0.f, lvsv = -INFINITY, ivsv = 0.f;
+  auto load_chunk = [&](int c) {  // compute side
+    c_chunk = c;
+    const int32_t id = page_id(64 * c + lane);
+    const bool ok = id >= 0;
+    const float vs = ok ? p_scale * a.v_scale[id] : 1.f;
+    idv = id;
+    ksv = ok ? a.k_scale[id] : 0.f;
+    lvsv = ok ? __builtin_amdgcn_logf(vs) : -INFINITY;
+    ivsv = ok ? __builtin_amdgcn_rcpf(vs) : 0.f;
+    asm volatile("" ::"v"(idv), "v"(ksv), "v"(lvsv), "v"(ivsv));
   };
   // this wave's loads of a tile: u = i*4 + wave; K loads first (D/16 of them),
   // then V; each covers 64 lanes x 16 B of one page
@@ -1017,6 +1039,18 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
         }
   }
   const float sc = a.scale * kLog2e * sq;
+  // page selector: row r < 4 of this A operand is 1.0 (E4M3 0x38) on the keys
+  // of page r and zero elsewhere, so selector . P^T gives each page's sum of
+  // rounded weights; a lane of group g holds keys 32g .. 32g+31 (pages 2g, 2g+1)
+  i32x8 sel;
+  {
+    const int w0 = col == 2 * half ? 0x38383838 : 0, w1 = col == 2 * half + 1 ? 0x38383838 : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sel[k] = w0;
+      sel[4 + k] = w1;
+    }
+  }
   float m = -INFINITY, l = 0.f, lq = 0.f, mu = 0.f;  // lq: sum of the rounded weights
   f32x16 acc[D / 32];
 #pragma unroll
@@ -1048,15 +1082,23 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     st_cur = st_cur == 2 ? 0 : st_cur + 1;
     st_pre = st_pre == 2 ? 0 : st_pre + 1;
 
-    float fac[4], vsc[4];
+    // per page: score factor, log2 of the P code factor and its inverse
+    // (pages without keys: weight 0 through a -inf exponent offset)
+    float fac[4], lvs[4], ivs[4];
+    bool okp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int32_t id = page_at(kt, j);
-      fac[j] = id < 0 ? 0.f : sc * a.k_scale[id];
-      vsc[j] = id < 0 ? 0.f : p_scale * a.v_scale[id];
+      const int pj = (4 * kt + j) & 63;
+      if (((4 * kt + j) >> 6) != c_chunk) load_chunk((4 * kt + j) >> 6);
+      okp[j] = __builtin_amdgcn_readlane(idv, pj) >= 0;
+      fac[j] = okp[j] ? sc * __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                   __builtin_bit_cast(int, ksv), pj))
+                      : 1.f;
+      lvs[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lvsv), pj));
+      ivs[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ivsv), pj));
     }
 
-    // S^T = K . Q^T for keys 32*beta .. +31 of the tile
+    // S^T = K . Q^T for keys 32*beta .. +31 of the tile, Q's two parts
     f32x16 sacc[2] = {};
     const int8_t* kb = reinterpret_cast<const int8_t*>(stg);
 #pragma unroll
@@ -1077,12 +1119,12 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
         sacc[beta] = mfma_fp8_b16th(kaa, ql[ks], sacc[beta]);
       }
     }
-    // value v of block beta is key 32*beta + 8*(v/4) + 4*half + v%4, page 2*beta + v/8
+    // value i = 16*beta + v is key 32*beta + 8*(v/4) + 4*half + v%4, on page i / 8
     float sv[32];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sv[16 * beta + v] = sacc[beta][v] * fac[2 * beta + (v >> 3)];
+      for (int v = 0; v < 16; ++v) sv[16 * beta + v] = sacc[beta][v];
     if (kt >= n_full) {
       const int lim = key_lim - kt * KT - 4 * half;
 #pragma unroll
@@ -1091,11 +1133,19 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
         sv[i] = off <= lim ? sv[i] : -INFINITY;
       }
     }
-    float mt = sv[0];
+    // row max over the tile: per page raw maxima times the (positive) factors
+    float mt = -INFINITY;
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mt = fmaxf(mt, sv[i]);
+    for (int j = 0; j < 4; ++j) {
+      float pm = fmaxf(fmaxf(sv[8 * j], sv[8 * j + 1]), sv[8 * j + 2]);
+      pm = fmaxf(fmaxf(pm, sv[8 * j + 3]), sv[8 * j + 4]);
+      pm = fmaxf(fmaxf(pm, sv[8 * j + 5]), sv[8 * j + 6]);
+      pm = fmaxf(pm, sv[8 * j + 7]);
+      mt = fmaxf(mt, okp[j] ? pm * fac[j] : -INFINITY);
+    }
     mt = max_xor32(mt);
-    if (__any(mt > m)) {  // exact running max: every weight <= 1 fills E4M3's range
+    // lazy rescale with headroom 2^2: every weight stays <= 4
+    if (__any(mt > m + 2.f)) {
       const float m_new = fmaxf(m, mt);
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
       l *= alpha;
@@ -1105,27 +1155,27 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       m = m_new;
       mu = m == -INFINITY ? 0.f : m;
     }
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    // weights times their page's code factor, straight from the exponent
+    float off_j[4];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      sv[i] = fast_exp2(sv[i] - mu);
-      ps[i & 3] += sv[i];
+    for (int j = 0; j < 4; ++j) off_j[j] = lvs[j] - mu;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], fac[i >> 3], off_j[i >> 3]));
+    {
+      float ps[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[j] = ((sv[8 * j] + sv[8 * j + 1]) + (sv[8 * j + 2] + sv[8 * j + 3])) +
+                ((sv[8 * j + 4] + sv[8 * j + 5]) + (sv[8 * j + 6] + sv[8 * j + 7]));
+      l += (ps[0] * ivs[0] + ps[1] * ivs[1]) + (ps[2] * ivs[2] + ps[3] * ivs[3]);
     }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // P^T codes as the B operand: group g takes keys 32g .. 32g+31
     i32x8 pb;
-    float pq[4] = {0.f, 0.f, 0.f, 0.f};  // rounded weights (code values) summed per page
 #pragma unroll
     for (int bq = 0; bq < 4; ++bq) {
-      const float s0 = vsc[bq >> 1], s1 = vsc[2 + (bq >> 1)];
-      const uint32_t d0 = fp8x4(sv[4 * bq] * s0, sv[4 * bq + 1] * s0, sv[4 * bq + 2] * s0, sv[4 * bq + 3] * s0);
-      const uint32_t d1 = fp8x4(sv[16 + 4 * bq] * s1, sv[16 + 4 * bq + 1] * s1, sv[16 + 4 * bq + 2] * s1,
-                                sv[16 + 4 * bq + 3] * s1);
-      const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8(d0, false), c1 = __builtin_amdgcn_cvt_pk_f32_fp8(d0, true);
-      const auto c2 = __builtin_amdgcn_cvt_pk_f32_fp8(d1, false), c3 = __builtin_amdgcn_cvt_pk_f32_fp8(d1, true);
-      pq[bq >> 1] += (c0[0] + c0[1]) + (c1[0] + c1[1]);
-      pq[2 + (bq >> 1)] += (c2[0] + c2[1]) + (c3[0] + c3[1]);
+      const uint32_t d0 = fp8x4(sv[4 * bq], sv[4 * bq + 1], sv[4 * bq + 2], sv[4 * bq + 3]);
+      const uint32_t d1 = fp8x4(sv[16 + 4 * bq], sv[16 + 4 * bq + 1], sv[16 + 4 * bq + 2], sv[16 + 4 * bq + 3]);
       const auto e = __builtin_amdgcn_permlane32_swap(d0, d1, false, false);
       pb[2 * bq] = static_cast<int>(e[0]);
       pb[2 * bq + 1] = static_cast<int>(e[1]);
@@ -1145,10 +1195,12 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       }
       acc[db] = mfma_fp8(va, pb, acc[db]);
     }
-    // back to weights: code sum of page j over its factor vsc[j] (0 for pages
-    // without keys, whose codes are 0)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lq += vsc[j] > 0.f ? pq[j] / vsc[j] : 0.f;
+    // rounded weights: rows 0..3 (values 0..3 of group 0's lanes) are the page
+    // sums of the codes; group 1's lanes hold rows 4..7, which are zero
+    {
+      const f32x16 qs = mfma_fp8(sel, pb, f32x16{});
+      lq += (qs[0] * ivs[0] + qs[1] * ivs[1]) + (qs[2] * ivs[2] + qs[3] * ivs[3]);
+    }
     if (kt + 2 < n_kt) wait_vmcnt<NI>(); else wait_vmcnt<0>();
     __syncthreads();
   }
@@ -1157,9 +1209,9 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
   l = sum_xor32(l);
   lq = sum_xor32(lq);
   if (!row_ok) return;
-  // acc holds codes: times sv_max / 448 it is sum(w V); write_rows divides
+  // acc holds codes: times sv_max / 112 it is sum(w V); write_rows divides
   // by l, so fold l / lq in to divide by the rounded weights' sum instead
-  const float back = sv_max * (1.f / 448.f) * (lq > 0.f ? l / lq : 0.f);
+  const float back = sv_max * (1.f / 112.f) * (lq > 0.f ? l / lq : 0.f);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] *= back;
   write_rows<D>(a, acc, m, l, qrow, split, half);

@@ -327,12 +327,13 @@ FP8MMA_CASES = [
 def _fp8_products_check(opool, wl, call, o, lse, ro, rl):
     """Bars of the fp8-product path, from E4M3's rounding.
 
-    Each weight w_i reaches P.V as E4M3 code w_i f_i (f_i = 448 times its V
-    page scale over the largest), so the kernel's weights are w_i (1 + e_i) with
+    Each weight w_i (at most 4 under the kernel's lazy rescale, the largest at
+    least 1) reaches P.V as E4M3 code w_i f_i (f_i = 112 times its V page scale
+    over the largest), so the kernel's weights are w_i (1 + e_i) with
     |e_i| <= 2^-4 for normal codes and |w_i e_i| <= 2^-10 / f_i below them; it
     divides by their own sum, so per feature d
         |O'_d - O_d| <= (2^-4 + n 2^-10 / f_min) / (1 - 2^-4) * max_i |v_id - O_d|
-    over the row's n visible keys (the largest weight is 1).  1e-2 is added for
+    over the row's n visible keys.  1e-2 is added for
     the rest: the remainder of Q after its two E4M3 parts, bf16 output
     rounding, fp32 sums.  The error averages down like 1/sqrt(keys), so rows
     that see 16 keys or more are held to the fp8-KV bound itself, and every
@@ -350,7 +351,7 @@ def _fp8_products_check(opool, wl, call, o, lse, ro, rl):
             continue
         bt = call.block_table[b].numpy()
         vs = np.array([opool.v_scale[bt[p]] for p in range((c + 15) // 16)])
-        f_min = 448.0 * vs.min() / vs.max()
+        f_min = 112.0 * vs.min() / vs.max()
         pos = c - n + np.arange(n)
         nk = np.minimum(pos + 1, c) if call.causal else np.full(n, c)
         for g in range(wl.num_kv_heads):
