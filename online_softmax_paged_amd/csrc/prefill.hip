@@ -704,20 +704,24 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     float sv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = s[i];
-    if (kt >= n_full) {
+    // one uniform branch for both masks: keys past the row's last visible key,
+    // and keys before key_begin (key_begin % 32 == 16: the first tile's first page)
+    if (kt >= n_full || kt * kKeys < a.key_begin) {
       const int lim = key_lim - kt * kKeys - 4 * half;
+      const int lo = a.key_begin - kt * kKeys - 4 * half;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? sv[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        sv[i] = off <= lim && off >= lo ? sv[i] : -INFINITY;
+      }
     }
-    if (kt * kKeys < a.key_begin) {  // key_begin % 32 == 16: the tile's first page is left out
+    // IEEE maximum: no operand canonicalisation (no NaN can arise here)
+    auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+    float mt = mx(mx(sv[0], sv[1]), sv[2]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sv[i] = -INFINITY;
-    }
-    float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sv[i]), sv[i + 1]);
-    mt = fmaxf(mt, sv[15]);
-    mt = max_xor32(mt);
+    for (int i = 3; i < 15; i += 2) mt = mx(mx(mt, sv[i]), sv[i + 1]);
+    mt = mx(mt, sv[15]);
+    mt = maxm_xor32(mt);
     const float mt_s = mt * sc;
     if (__any(mt_s > m + 8.f)) {
       const float m_new = fmaxf(m, mt_s);
@@ -953,44 +957,35 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     const bool ok = id >= 0;
     const float vs = ok ? p_scale * a.v_scale[id] : 1.f;
     idv = id;
-    ksv = ok ? a.k_scale[id] : 0.f;
+    ksv = ok ? a.k_scale[id] : 1.f;
     lvsv = ok ? __builtin_amdgcn_logf(vs) : -INFINITY;
     ivsv = ok ? __builtin_amdgcn_rcpf(vs) : 0.f;
     asm volatile("" ::"v"(idv), "v"(ksv), "v"(lvsv), "v"(ivsv));
   };
-  // this wave's loads of a tile: u = i*4 + wave; K loads first (D/16 of them),
-  // then V; each covers 64 lanes x 16 B of one page
-  uint32_t voff[NI];
+  // this wave's loads of a tile: all of page 4t + wave, D/64 loads of its K
+  // rows, then D/64 of its V (64 lanes x 16 B each)
+  constexpr int LP = D / 64;
+  uint32_t kvo[LP], vvo[LP];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int u = i * 4 + wave;
-    if (u < D / 16) {
-      const int m = u * 64 + lane, key = m / CK, pos = m % CK, c = pos ^ (key % CK);
-      voff[i] = static_cast<uint32_t>((key % kPage) * D + c * 16);
-    } else {
-      voff[i] = static_cast<uint32_t>(((u - D / 16) * 64 + lane) % D * 16);
-    }
+  for (int h = 0; h < LP; ++h) {
+    const int m = h * 64 + lane, kip = m / CK, pos = m % CK;
+    kvo[h] = static_cast<uint32_t>(kip * D + (pos ^ (kip % CK)) * 16);
+    vvo[h] = static_cast<uint32_t>(h * 1024 + lane * 16);
   }
   const uint32_t lds0 = lds_address(sm.buf);
   auto dma_tile = [&](int t, uint32_t stage) {
-    int32_t ph[4];
-    int nv[4];
+    const int32_t id = page_at(t, wave);
+    const int nv = min(kPage, max(0, ctx - (4 * t + wave) * kPage));
+    const int64_t chunk = (static_cast<int64_t>(id < 0 ? 0 : id) * Hkv + g) * (kPage * D);
+    const int32_t knb = id < 0 ? 0 : nv * D;
+    const int32_t vnb = id < 0 || nv == 0 ? 0 : kPage * D;
+    const uint32_t dst = stage + wave * (kPage * D);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ph[j] = page_at(t, j);
-      nv[j] = min(kPage, max(0, ctx - (4 * t + j) * kPage));
-    }
+    for (int h = 0; h < LP; ++h)
+      dma16(static_cast<const char*>(a.k) + chunk, knb, kvo[h], dst + h * 1024);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int u = i * 4 + wave;
-      const bool is_v = u >= D / 16;
-      const int pj = is_v ? (u - D / 16) * 64 / D : (u * 64 / CK) / kPage;
-      const int32_t id = ph[pj];
-      const int64_t chunk = (static_cast<int64_t>(id < 0 ? 0 : id) * Hkv + g) * (kPage * D);
-      const int32_t nb = id < 0 ? 0 : (is_v ? (nv[pj] > 0 ? kPage * D : 0) : nv[pj] * D);
-      const char* base = static_cast<const char*>(is_v ? a.v : a.k) + chunk;
-      dma16(base, nb, voff[i], stage + u * 1024);
-    }
+    for (int h = 0; h < LP; ++h)
+      dma16(static_cast<const char*>(a.v) + chunk, vnb, vvo[h], dst + Fp8Smem<D>::KB + h * 1024);
   };
   if (kt_begin < n_kt) {
     dma_tile(kt_begin, lds0);
@@ -1084,18 +1079,17 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
 
     // per page: score factor, log2 of the P code factor and its inverse
     // (pages without keys: weight 0 through a -inf exponent offset)
-    float fac[4], lvs[4], ivs[4];
-    bool okp[4];
+    // (an absent page: factor 1, and -inf added to its max and exponents)
+    float fac[4], lvs[4], ivs[4], madd[4];
+    if (((4 * kt) >> 6) != c_chunk) load_chunk((4 * kt) >> 6);  // a tile's 4 pages share a chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pj = (4 * kt + j) & 63;
-      if (((4 * kt + j) >> 6) != c_chunk) load_chunk((4 * kt + j) >> 6);
-      okp[j] = __builtin_amdgcn_readlane(idv, pj) >= 0;
-      fac[j] = okp[j] ? sc * __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                   __builtin_bit_cast(int, ksv), pj))
-                      : 1.f;
+      const float ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ksv), pj));
       lvs[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lvsv), pj));
       ivs[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ivsv), pj));
+      fac[j] = sc * ks;
+      madd[j] = lvs[j] == -INFINITY ? -INFINITY : 0.f;
     }
 
     // S^T = K . Q^T for keys 32*beta .. +31 of the tile, Q's two parts
@@ -1134,16 +1128,18 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       }
     }
     // row max over the tile: per page raw maxima times the (positive) factors
+    // (IEEE maximum: no operand canonicalisation, and no NaN can arise here)
+    auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
     float mt = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float pm = fmaxf(fmaxf(sv[8 * j], sv[8 * j + 1]), sv[8 * j + 2]);
-      pm = fmaxf(fmaxf(pm, sv[8 * j + 3]), sv[8 * j + 4]);
-      pm = fmaxf(fmaxf(pm, sv[8 * j + 5]), sv[8 * j + 6]);
-      pm = fmaxf(pm, sv[8 * j + 7]);
-      mt = fmaxf(mt, okp[j] ? pm * fac[j] : -INFINITY);
+      float pm = mx(mx(sv[8 * j], sv[8 * j + 1]), sv[8 * j + 2]);
+      pm = mx(mx(pm, sv[8 * j + 3]), sv[8 * j + 4]);
+      pm = mx(mx(pm, sv[8 * j + 5]), sv[8 * j + 6]);
+      pm = mx(pm, sv[8 * j + 7]);
+      mt = mx(mt, __builtin_fmaf(pm, fac[j], madd[j]));
     }
-    mt = max_xor32(mt);
+    mt = maxm_xor32(mt);
     // lazy rescale with headroom 2^2: every weight stays <= 4
     if (__any(mt > m + 2.f)) {
       const float m_new = fmaxf(m, mt);
