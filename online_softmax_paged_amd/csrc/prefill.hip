@@ -437,23 +437,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 
 // Block ids of one tile, read raw (clamped index, no checks) so nothing waits
 // on the load until the ids are used an iteration later.
-struct RawPages {
-  int32_t id[2];
-};
-
-__device__ __forceinline__ TilePages check_pages(const AttnArgs& a, const RawPages& r, int t,
-                                                 int n_pages) {
-  TilePages tp;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int32_t phys = 2 * t + j < n_pages ? r.id[j] : -1;
-    tp.phys[j] = phys;
-    tp.ok[j] = phys >= 0 && phys < a.num_blocks;
-    tp.ks[j] = tp.vs[j] = 1.f;
-  }
-  return tp;
-}
-
 template <int D>
 struct DmaSmem {
   static constexpr int KB = kKeys * D * 2;      // K tile bytes
@@ -508,21 +491,13 @@ struct DmaPlan {
 };
 
 
+// One tile's DMA: off[j] is page j's (page, KV head) byte offset in the
+// pools, knb[j] / vnb[j] the bytes of its K rows / V^T page to move (0 for an
+// absent page; reads past them return zero).
 template <int D, int NW>
-__device__ __forceinline__ void dma_tile(const AttnArgs& a, int g, const TilePages& tp, int t,
-                                         int ctx, uint32_t stage, const DmaPlan<D, NW>& plan) {
-  constexpr int PAGE_BYTES = kPage * D * 2;
-  int64_t off[2];
-  int knb[2], vnb[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tok0 = t * kKeys + j * kPage;
-    const bool ok = tp.ok[j];
-    const int n_valid = min(kPage, max(0, ctx - tok0));
-    off[j] = ok ? (static_cast<int64_t>(tp.phys[j]) * a.num_kv_heads + g) * PAGE_BYTES : 0;
-    knb[j] = ok ? n_valid * D * 2 : 0;
-    vnb[j] = ok && n_valid > 0 ? PAGE_BYTES : 0;
-  }
+__device__ __forceinline__ void dma_tile(const AttnArgs& a, const uint64_t (&off)[2],
+                                         const int (&knb)[2], const int (&vnb)[2], uint32_t stage,
+                                         const DmaPlan<D, NW>& plan) {
 #pragma unroll
   for (int i = 0; i < DmaPlan<D, NW>::NI; ++i) {
     if (DmaPlan<D, NW>::NI * NW != DmaPlan<D, NW>::TOT && i >= plan.count) break;
@@ -622,27 +597,45 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
 
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  // Block ids of 64 consecutive pages, one per lane, refreshed every 32
-  // tiles; a tile's two ids are then register reads, not memory loads.
-  int id_chunk = 0;
-  int32_t idv = lane < n_pages ? bt[lane] : -1;
-  auto tile_pages = [&](int t) -> TilePages {
-    const int c = (2 * t) >> 6;
-    if (c != id_chunk) {  // uniform; at most once per 32 tiles
-      id_chunk = c;
-      idv = 64 * c + lane < n_pages ? bt[64 * c + lane] : -1;
+  // 64 consecutive pages in lane vectors, refreshed every 32 tiles: each
+  // lane holds its page's (page, KV head) byte offset in the pools and the
+  // bytes of its K rows | V^T page << 16 to move (0 for an absent page), so a
+  // tile's DMA arguments are register reads, not memory loads and products.
+  constexpr int PAGE_BYTES = kPage * D * 2;
+  int pg_chunk = -1;
+  uint32_t po_lo = 0, po_hi = 0, pnb = 0;
+  auto dma = [&](int t, uint32_t stage) {
+    const int c = (2 * t) >> 6;  // a tile's two pages share a chunk
+    if (c != pg_chunk) {         // uniform; at most once per 32 tiles
+      pg_chunk = c;
+      const int p = 64 * c + lane;
+      const int32_t id = p < n_pages ? bt[p] : -1;
+      const bool ok = id >= 0 && id < a.num_blocks;
+      const uint64_t o = ok ? (static_cast<uint64_t>(id) * Hkv + g) * PAGE_BYTES : 0;
+      const int nv = min(kPage, max(0, ctx - p * kPage));
+      po_lo = static_cast<uint32_t>(o);
+      po_hi = static_cast<uint32_t>(o >> 32);
+      pnb = ok ? static_cast<uint32_t>(nv * D * 2) | (nv > 0 ? uint32_t(PAGE_BYTES) << 16 : 0u) : 0u;
       // consume the load here, so its wait stays inside this rare branch
-      asm volatile("" ::"v"(idv));
+      asm volatile("" ::"v"(po_lo), "v"(po_hi), "v"(pnb));
     }
-    RawPages r;
-    r.id[0] = __builtin_amdgcn_readlane(idv, (2 * t) & 63);
-    r.id[1] = __builtin_amdgcn_readlane(idv, (2 * t + 1) & 63);
-    return check_pages(a, r, t, n_pages);
+    uint64_t off[2];
+    int knb[2], vnb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = (2 * t + j) & 63;
+      off[j] = (static_cast<uint64_t>(__builtin_amdgcn_readlane(po_hi, q)) << 32) |
+               static_cast<uint32_t>(__builtin_amdgcn_readlane(po_lo, q));
+      const uint32_t nb = __builtin_amdgcn_readlane(pnb, q);
+      knb[j] = static_cast<int>(nb & 0xffffu);
+      vnb[j] = static_cast<int>(nb >> 16);
+    }
+    dma_tile<D, NW>(a, off, knb, vnb, stage, plan);
   };
   const uint32_t lds0 = lds_address(sm.buf);
   if (kt_begin < n_kt) {  // uniform; an empty split moves nothing
-    dma_tile<D, NW>(a, g, tile_pages(kt_begin), kt_begin, ctx, lds0, plan);
-    dma_tile<D, NW>(a, g, tile_pages(kt_begin + 1), kt_begin + 1, ctx, lds0 + STAGE, plan);
+    dma(kt_begin, lds0);
+    dma(kt_begin + 1, lds0 + STAGE);
   }
 
   bf16x8 qf[D / 16];
@@ -684,7 +677,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     }
     // DMA tile kt+2 into the stage tile kt-1 used (all waves are past it)
     if (kt + 2 < n_kt)
-      dma_tile<D, NW>(a, g, tile_pages(kt + 2), kt + 2, ctx, lds0 + st_pre * STAGE, plan);
+      dma(kt + 2, lds0 + st_pre * STAGE);
     st_cur = st_cur == 2 ? 0 : st_cur + 1;
     st_pre = st_pre == 2 ? 0 : st_pre + 1;
 
