@@ -204,14 +204,23 @@ pa_status pa_prefill(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, vo
  * pa_prefill for an fp8 pool with both products on the fp8 matrix cores
  * (FlashAttention-3's low-precision forward: the survey page, FlashAttention-3
  * section), the cache's per-page scales kept exact:
- *   - each query row is quantised to E4M3 with its own scale amax/448;
- *   - S = (Q codes . K codes) * q scale * K page scale, in fp32;
- *   - the online softmax runs in fp32 as in pa_prefill; each weight P (<= 2^8)
- *     is multiplied by its key's V page scale over the largest V page scale
- *     of the workgroup's keys and by 448/256, rounded to E4M3, and
- *     multiplied with the V codes; the row sum uses the unrounded weights.
- * So Q and P each carry E4M3 rounding (relative 2^-4) on top of the pool's;
- * results stay within the fp8-KV bound of 6e-2 on the library's tests.
+ *   - each query row x gets one scale s = amax/448 and is split into two E4M3
+ *     parts, hi = E4M3(x/s) and lo = E4M3(16 (x/s - hi)), so Q enters the
+ *     scores to about 2^-8 relative;
+ *   - S = Q . K codes * K page scale, in fp32;
+ *   - the online softmax runs in fp32; each weight (<= 4 under a lazy
+ *     rescale) times 112 times its key's V page scale over the largest V
+ *     page scale of the workgroup's keys is rounded to E4M3 and multiplied
+ *     with the V codes;
+ *   - O is divided by the sum of those rounded weights, LSE uses the sum of
+ *     the unrounded ones.
+ * So every weight carries E4M3 rounding (relative 2^-4) on top of the pool's,
+ * and O is the weighted mean of V under weights each within 2^-4 of exact:
+ * per element |dO| <= (1/15) * the spread of the row's visible V values in
+ * that feature, plus terms below 1e-2.  The error averages down with the keys
+ * a row sees: on the library's tests rows that see 16 keys or more, and every
+ * LSE, stay within the fp8-KV bound of 6e-2; rows that see fewer may not
+ * (pa_prefill keeps them at the pool's own precision).
  * Arguments, layouts, key splits, workspace and errors as pa_prefill, except:
  * the pool must be PA_FP8_E4M3 (else PA_ERR_UNSUPPORTED), q bf16.
  */
