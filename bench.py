@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -400,6 +401,46 @@ def one_call_timings(pa, wl, pool, dev, args, scratch):
     return out
 
 
+def measured_ceilings(pa, dev) -> dict:
+    """What this GPU sustains, measured in the same process with the library's
+    probes (pa_probe_stream_read, pa_probe_mfma): the best of three grid sizes
+    for a non-temporal streaming read of 1 GiB, and MFMA loops of 4
+    independent chains per wave on register operands (bf16 and fp8)."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    best = 0.0
+    for blocks in (1024, 2048, 4096):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        sec = timed(lambda: pa.probe_stream_read(buf, blocks=blocks, out=out), 10)
+        best = max(best, buf.numel() / sec / 1e9)
+    del buf
+    res = {"hbm_read_gbps": best}
+    out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    for dt, iters in (("bf16", 2000), ("fp8", 1000)):
+        flop = [0.0]
+
+        def run():
+            flop[0] = pa.probe_mfma(dt, blocks=2048, iters=iters, out=out)
+        sec = timed(run, 3)
+        res[f"mfma_{dt}_tflops"] = flop[0] / sec / 1e12
+    res["method"] = ("library probes in this process: non-temporal streaming read of 1 GiB "
+                     "(best of 1024/2048/4096 workgroups); 4 independent MFMA chains per wave "
+                     "on register operands, 2048 workgroups")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -418,6 +459,8 @@ def main():
                     help="prefill calls on fp8 pools use pa_prefill (codes widened to bf16, "
                          "products on the bf16 matrix cores) instead of pa_prefill_fp8 (Q and "
                          "P in E4M3, both products on the fp8 matrix cores)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (streaming read, MFMA loops) after the timed steps")
     ap.add_argument("--one-call", action="store_true",
                     help="also time a shared-prefix workload's calls joined into one call "
                          "(pa_prefill and pa_prefill_shared_prefix), outside the step")
@@ -535,8 +578,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_launch_ms = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)) / args.steps
-                     for i in range(len(launches))]
+    step_ms = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
+               for i in range(len(launches))]
+    per_launch_ms = [sum(x) / len(x) for x in step_ms]
     # with a flush between steps the step time is the sum of the launches'
     # event times; otherwise it is the wall clock of the K steps
     ms_per_step = sum(per_launch_ms) if scratch is not None else wall * 1e3 / args.steps
@@ -544,7 +588,8 @@ def main():
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)"}
     parts = {}
-    for (kind, wl, call, _, f8), ms in zip(launches, per_launch_ms):
+    for (kind, wl, call, _, f8), ms, sms in zip(launches, per_launch_ms, step_ms):
+        spread = {"ms_median": statistics.median(sms), "ms_min": min(sms)}
         if kind == "prefill":
             fl = prefill_flops(call, wl.head_dim, wl.num_q_heads)
             tf = fl / (ms * 1e-3) / 1e12
@@ -552,13 +597,13 @@ def main():
                 {"workload": wl.name, "ms": ms, "tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
                  "products": "fp8" if f8 else "bf16",
                  "frac_products_peak": tf / (PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS),
-                 "flops": fl, "dtype": wl.kv_dtype})
+                 "flops": fl, "dtype": wl.kv_dtype, **spread})
         else:
             by = decode_kv_bytes(call, wl)
             gbps = by / (ms * 1e-3) / 1e9
             parts.setdefault("decode", []).append(
                 {"workload": wl.name, "ms": ms, "gbps": gbps, "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
-                 "kv_bytes": by, "dtype": wl.kv_dtype})
+                 "kv_bytes": by, "dtype": wl.kv_dtype, **spread})
     pre = parts.get("prefill", [])
     dec = parts.get("decode", [])
     if pre:
@@ -593,6 +638,19 @@ def main():
         result["decode"] = {"value": sum(x["kv_bytes"] for x in dec) / (sum(x["ms"] for x in dec) * 1e-3) / 1e9,
                             "unit": "GB/s", "frac_hbm_peak": None}
         result["decode"]["frac_hbm_peak"] = result["decode"]["value"] / PEAK_HBM_GBPS
+    if not args.no_ceilings:
+        ceil = measured_ceilings(pa, dev)
+        result["ceilings"] = ceil
+        for key in ("roofline", "roofline_decode"):
+            r = result.get(key)
+            if not r:
+                continue
+            if r["bound"] == "hbm":
+                m = ceil["hbm_read_gbps"]
+            else:
+                m = ceil["mfma_fp8_tflops" if r["peak"] == PEAK_FP8_TFLOPS else "mfma_bf16_tflops"]
+            r["measured_peak"] = m
+            r["frac_measured"] = r["achieved"] / m
     if args.one_call:
         for wl in wls:
             if wl.shared_prefix and len(wl.calls) > 1:
@@ -602,8 +660,13 @@ def main():
         cb = cpu_baseline(wls, args.cpu_budget)
         first = cb.get("prefill") or cb.get("decode")
         result["cpu_baseline"] = dict(first)
+        if first.get("value"):
+            result["cpu_baseline"]["gpu_over_oracle"] = result["value"] / first["value"]
         if "prefill" in cb and "decode" in cb:
-            result["cpu_baseline"]["decode"] = cb["decode"]
+            result["cpu_baseline"]["decode"] = dict(cb["decode"])
+            if cb["decode"].get("value") and "decode" in result:
+                result["cpu_baseline"]["decode"]["gpu_over_oracle"] = \
+                    result["decode"]["value"] / cb["decode"]["value"]
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -404,6 +404,30 @@ pa_status pa_plan_append(pa_allocator* a, int32_t* block_table, int32_t bt_strid
                          int32_t* slot_mapping, int32_t* copy_src, int32_t* copy_dst,
                          int32_t max_copies, int32_t* num_copies);
 
+/* ------------------------------------------------------------ measurement probes
+ * Not part of the attention path.  Two kernels that measure what this GPU
+ * sustains, so that each attention kernel's rate can be read against a
+ * measured ceiling as well as the spec peak (the survey's measurement section
+ * asks for both; bench.py runs these beside the attention kernels).
+ *
+ * pa_probe_stream_read: every 16-byte word of buf (device memory, bytes a
+ *   multiple of 16) is read once with non-temporal loads by `blocks`
+ *   workgroups of 256 threads in a grid-stride loop; out (device,
+ *   blocks * 256 uint32) receives one XOR per thread of the words it read.
+ * pa_probe_mfma: `blocks` workgroups of 4 waves; each wave runs 4 independent
+ *   chains of `iters` MFMAs on register operands.  PA_BF16 uses
+ *   v_mfma_f32_32x32x16_bf16 (32768 FLOP each), PA_FP8_E4M3
+ *   v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales (131072 FLOP
+ *   each); out (device, blocks * 256 float) receives each thread's sum of its
+ *   accumulators.  FLOP per call: blocks * 16 * iters * the instruction's.
+ * Errors: PA_ERR_INVALID_ARG for null pointers, bytes 0 or not a multiple of
+ * 16, blocks outside [1, 65535], iters < 1; PA_ERR_UNSUPPORTED for another
+ * dtype; PA_ERR_LAUNCH when the launch fails.  Stream-ordered on `stream`.
+ */
+pa_status pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
+                               void* stream);
+pa_status pa_probe_mfma(pa_dtype dtype, float* out, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

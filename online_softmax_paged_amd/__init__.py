@@ -87,6 +87,8 @@ _append = _sig("pa_append_kv", ctypes.c_int, [_P, _VP, _VP, ctypes.c_int, _VP, _
 _copy_blocks = _sig("pa_copy_blocks", ctypes.c_int, [_P, _VP, _VP, _I32, _VP])
 _plan_append = _sig("pa_plan_append", ctypes.c_int,
                     [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP])
+_probe_read = _sig("pa_probe_stream_read", ctypes.c_int, [_VP, _SZ, _VP, _I32, _VP])
+_probe_mfma = _sig("pa_probe_mfma", ctypes.c_int, [ctypes.c_int, _VP, _I32, _I32, _VP])
 
 EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes", "pa_write_kv",
             "pa_gather_kv", "pa_prefill", "pa_decode_num_splits", "pa_decode_workspace_bytes",
@@ -96,7 +98,8 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_prefill_workspace_bytes", "pa_shared_prefix_num_splits",
             "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
             "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits",
-            "pa_backward_workspace_bytes", "pa_prefill_backward", "pa_prefill_fp8"]
+            "pa_backward_workspace_bytes", "pa_prefill_backward", "pa_prefill_fp8",
+            "pa_probe_stream_read", "pa_probe_mfma"]
 
 DECODE_BALANCED = -1
 
@@ -512,3 +515,28 @@ class BlockAllocator:
                             ctypes.byref(nc)), "pa_plan_append")
         k = int(nn.sum())
         return slots[:k], csrc[:nc.value], cdst[:nc.value]
+
+
+# ------------------------------------------------------------ measurement probes
+def probe_stream_read(buf: torch.Tensor, blocks: int = 2048, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Read every byte of the contiguous device tensor buf once (pa_probe_stream_read);
+    returns the per-thread XORs (int32 [blocks * 256])."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    _check(_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), blocks,
+                       _stream(stream)), "pa_probe_stream_read")
+    return out
+
+
+PROBE_MFMA_FLOP = {"bf16": 32 * 32 * 16 * 2, "fp8": 32 * 32 * 64 * 2}
+
+
+def probe_mfma(dtype: str = "bf16", blocks: int = 2048, iters: int = 2000,
+               out: torch.Tensor | None = None, stream=None) -> float:
+    """Run the MFMA loop (pa_probe_mfma); returns the FLOP it performs."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    dt = {"bf16": PA_BF16, "fp8": PA_FP8_E4M3}[dtype]
+    _check(_probe_mfma(dt, _ptr(out), blocks, iters, _stream(stream)), "pa_probe_mfma")
+    return float(blocks) * 16 * iters * PROBE_MFMA_FLOP[dtype]

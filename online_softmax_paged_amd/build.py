@@ -18,7 +18,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "kv_cache.hip", "decode.hip", "prefill.hip", "backward.hip", "allocator.cpp"]
+SOURCES = ["api.hip", "kv_cache.hip", "decode.hip", "prefill.hip", "backward.hip", "probes.hip",
+           "allocator.cpp"]
 
 # Keep MFMA accumulators in ordinary VGPRs so the softmax can rescale them
 # without copies to and from the accumulation registers.

@@ -91,7 +91,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 6; }
+int32_t pa_abi_version(void) { return 7; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 6
+    assert pa.abi_version() == 7
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -248,6 +248,23 @@ def test_prefill_fp8_checks():
     assert call(f, splits=3) == pa.PA_ERR_WORKSPACE
     assert call(f, max_q=0) == pa.PA_ERR_INVALID_ARG
     assert call(f, B=0) == pa.PA_OK
+
+
+def test_probe_checks():
+    """Measurement probes reject bad arguments before any launch."""
+    rd = lambda buf, n, out, blocks: pa._probe_read(buf, n, out, blocks, None)
+    assert rd(0, 1 << 20, 0x2000, 64) == pa.PA_ERR_INVALID_ARG       # null buffer
+    assert rd(0x1000, 1 << 20, 0, 64) == pa.PA_ERR_INVALID_ARG       # null output
+    assert rd(0x1000, 1000, 0x2000, 64) == pa.PA_ERR_INVALID_ARG     # not a multiple of 16
+    assert rd(0x1000, 0, 0x2000, 64) == pa.PA_ERR_INVALID_ARG
+    assert rd(0x1000, 1 << 20, 0x2000, 0) == pa.PA_ERR_INVALID_ARG
+    assert rd(0x1000, 1 << 20, 0x2000, 65536) == pa.PA_ERR_INVALID_ARG
+    mf = lambda dt, out, blocks, iters: pa._probe_mfma(dt, out, blocks, iters, None)
+    assert mf(pa.PA_F32, 0x2000, 64, 10) == pa.PA_ERR_UNSUPPORTED
+    assert mf(pa.PA_BF16, 0, 64, 10) == pa.PA_ERR_INVALID_ARG
+    assert mf(pa.PA_BF16, 0x2000, 64, 0) == pa.PA_ERR_INVALID_ARG
+    assert mf(pa.PA_FP8_E4M3, 0x2000, 0, 10) == pa.PA_ERR_INVALID_ARG
+    assert pa.PROBE_MFMA_FLOP == {"bf16": 32768, "fp8": 131072}
 
 
 def test_decode_split_heuristic():
