@@ -444,8 +444,10 @@ def measured_ceilings(pa, dev) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the prefill reaches its steady rate only after some 50-100 ms of sustained
+    # load: timed after 5 warmup steps it runs ~8% slower than after 100
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
