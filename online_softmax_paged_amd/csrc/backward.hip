@@ -402,7 +402,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int b = pair / Hkv, g = pair % Hkv;
   const int q0 = a.cu_q_lens[b], qlen = a.cu_q_lens[b + 1] - q0;
   const int nrows = qlen * G;
-  const int W0 = y * 128;
+  // row blocks from the last one down: under a causal mask the last rows see
+  // the most keys, so the longest tasks start first
+  const int W0 = (gridDim.y - 1 - y) * 128;
   if (W0 >= nrows) return;
   const int ctx = clamp_ctx(a, b);
   const int pos_base = ctx - qlen;
