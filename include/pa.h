@@ -1,5 +1,6 @@
 /*
- * pa.h -- paged attention forward for MI355X (gfx950): C ABI.
+ * pa.h -- paged attention for MI355X (gfx950): C ABI (the forward pass, its
+ *         backward, the paged KV cache and its block allocator, measurement probes).
  *
  * Exact scaled-dot-product attention, softmax(scale * Q K^T) V, computed with
  * K/V tiles streamed from a paged KV cache and an online softmax (running max,
