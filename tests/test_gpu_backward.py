@@ -100,3 +100,33 @@ def test_backward_prefill_1x2048_sampled_against_oracle():
     call = wl.calls[0]
     do, dq, dk, dv = _run_backward(wl, call, seed=5)
     _check(wl, call, do, dq, dk, dv)
+
+
+def _random_cases(n, seed):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        D = rng.choice([64, 128])
+        Hkv = rng.choice([1, 2, 4])
+        G = rng.choice([1, 2, 4, 8])
+        B = rng.randint(1, 4)
+        ctx = [rng.choice([rng.randint(1, 40), rng.randint(1, 400), 16 * rng.randint(1, 20),
+                           32 * rng.randint(1, 12) + 1]) for _ in range(B)]
+        ql = [rng.choice([1, c, rng.randint(1, c)]) for c in ctx]
+        out.append((i, D, Hkv * G, Hkv, tuple(ctx), tuple(ql), rng.random() < 0.8))
+    return out
+
+
+@pytest.mark.parametrize("i,D,Hq,Hkv,ctx,ql,causal", _random_cases(8, 17),
+                         ids=lambda v: None)
+def test_backward_random_shapes(i, D, Hq, Hkv, ctx, ql, causal):
+    """A seeded random sweep of small shapes (head dims, group sizes, ragged
+    lengths, chunks of 1 token to the whole context, causal or not)."""
+    _log(f"backward random {i}: D={D} Hq={Hq} Hkv={Hkv} ctx={ctx} q={ql} causal={causal}")
+    wl = workloads.small("prefill", kv_dtype="bf16", q_dtype="bf16", num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=D, ctx_lens=ctx, q_lens=ql, seed=400 + i,
+                         causal=causal)
+    call = wl.calls[0]
+    do, dq, dk, dv = _run_backward(wl, call, seed=11 + i, causal=causal)
+    _check(wl, call, do, dq, dk, dv, causal)
