@@ -535,6 +535,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
+  const int krow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);  // col, bits 2 and 3 swapped
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
   // Workgroups are dealt to the 8 dies (XCDs, each with its own 4 MB L2)
   // round robin by linear id.  When the (sequence, KV head) pairs split evenly
@@ -690,12 +691,16 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     st_pre = st_pre == 2 ? 0 : st_pre + 1;
 
     // S^T = K . Q^T
-    const char* kbase = stg + col * (D * 2);
+    // Lane col feeds key krow = col with bits 2 and 3 swapped as row col of
+    // the MFMA, so that value i of a lane of half h is key
+    // 16(i/8) + 8h + 4((i/4)%2) + i%4: each lane then holds 8 consecutive keys
+    // per 16-key step, already the order of P.V's B operand (no lane swaps).
+    const char* kbase = stg + krow * (D * 2);
     bf16x8 kf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int logical = 2 * ks + half;
-      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + ((logical ^ (col % CPR)) * 16));
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + ((logical ^ (krow % CPR)) * 16));
     }
     f32x16 s = {};
 #pragma unroll
@@ -708,11 +713,11 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     // one uniform branch for both masks: keys past the row's last visible key,
     // and keys before key_begin (key_begin % 32 == 16: the first tile's first page)
     if (kt >= n_full || kt * kKeys < a.key_begin) {
-      const int lim = key_lim - kt * kKeys - 4 * half;
-      const int lo = a.key_begin - kt * kKeys - 4 * half;
+      const int lim = key_lim - kt * kKeys - 8 * half;
+      const int lo = a.key_begin - kt * kKeys - 8 * half;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int off = 8 * (i >> 2) + (i & 3);
+        const int off = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
         sv[i] = off <= lim && off >= lo ? sv[i] : -INFINITY;
       }
     }
@@ -745,15 +750,10 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     const char* vbase = stg + DmaSmem<D>::KB;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      // this lane holds keys 16c + 4*half + {0..3} (A) and 16c + 8 + 4*half + {0..3} (B);
-      // after the swaps: half 0 holds keys 16c + 0..7, half 1 holds 16c + 8..15
-      uint32_t A0 = pack_bf16x2(sv[8 * c + 0], sv[8 * c + 1]);
-      uint32_t A1 = pack_bf16x2(sv[8 * c + 2], sv[8 * c + 3]);
-      uint32_t B0 = pack_bf16x2(sv[8 * c + 4], sv[8 * c + 5]);
-      uint32_t B1 = pack_bf16x2(sv[8 * c + 6], sv[8 * c + 7]);
-      const auto r0 = __builtin_amdgcn_permlane32_swap(A0, B0, false, false);
-      const auto r1 = __builtin_amdgcn_permlane32_swap(A1, B1, false, false);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{r0[0], r1[0], r0[1], r1[1]});
+      // this lane holds keys 16c + 8*half + {0..7}, the B operand's order
+      const bf16x8 pf = __builtin_bit_cast(
+          bf16x8, u32x4{pack_bf16x2(sv[8 * c + 0], sv[8 * c + 1]), pack_bf16x2(sv[8 * c + 2], sv[8 * c + 3]),
+                        pack_bf16x2(sv[8 * c + 4], sv[8 * c + 5]), pack_bf16x2(sv[8 * c + 6], sv[8 * c + 7])});
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int d = db * 32 + col;
