@@ -834,7 +834,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(AttnArgs a) {
 //      weights.
 // Tiles of 64 keys (four pages; one 64-deep k-step for P.V).  K and V codes
 // move by buffer loads straight into LDS, three stages of 16 KiB (d = 128):
-//   K [64 keys][D/16 chunks of 16 B], chunk c of key i at c ^ (i % (D/16));
+//   K [64 keys][D/16 chunks of 16 B], chunk c of key i at c ^ fp8_ksw<D>(i);
 //   V per page [D][16 keys], as in the pool.
 // An operand lane of group g (lane / 32) holds k = 32g .. 32g+31 of each
 // 64-deep k-step in A and B alike (any common order contracts the same).
@@ -861,6 +861,19 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 // the same with B's block scale 2^-4 (E8M0 123)
 __device__ __forceinline__ f32x16 mfma_fp8_b16th(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 123);
+}
+
+// Chunk swizzle of K row `key` (0..63) of an fp8 tile: chunk c sits at
+// c ^ fp8_ksw<D>(key).  The score MFMA's lanes 0..15 read keys 0-3, 32-35,
+// 4-7, 36-39 (and so on), so keys of one bank row (same key % (128/D)) among
+// them get distinct swizzles: bits 1-2 and 5 of the key for d = 128, bits 2
+// and 5 for d = 64.
+template <int D>
+__device__ __forceinline__ int fp8_ksw(int key) {
+  if constexpr (D == 128)
+    return ((key >> 1) & 3) | (((key >> 5) & 1) << 2);
+  else
+    return ((key >> 2) & 1) | (((key >> 5) & 1) << 1);
 }
 
 template <int D>
@@ -970,7 +983,7 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
 #pragma unroll
   for (int h = 0; h < LP; ++h) {
     const int m = h * 64 + lane, kip = m / CK, pos = m % CK;
-    kvo[h] = static_cast<uint32_t>(kip * D + (pos ^ (kip % CK)) * 16);
+    kvo[h] = static_cast<uint32_t>(kip * D + (pos ^ fp8_ksw<D>(kPage * wave + kip)) * 16);
     vvo[h] = static_cast<uint32_t>(h * 1024 + lane * 16);
   }
   const uint32_t lds0 = lds_address(sm.buf);
@@ -1092,18 +1105,30 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       fac[j] = sc * ks;
       madd[j] = lvs[j] == -INFINITY ? -INFINITY : 0.f;
     }
+    // this lane's scores of block beta all lie on page 2*half + beta
+    float fb[2], lb[2], ib[2], mb[2];
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta) {
+      fb[beta] = half ? fac[2 + beta] : fac[beta];
+      lb[beta] = half ? lvs[2 + beta] : lvs[beta];
+      ib[beta] = half ? ivs[2 + beta] : ivs[beta];
+      mb[beta] = half ? madd[2 + beta] : madd[beta];
+    }
 
-    // S^T = K . Q^T for keys 32*beta .. +31 of the tile, Q's two parts
+    // S^T = K . Q^T, Q's two parts.  MFMA beta's row col is key
+    // 32*((col/4)%2) + 16*beta + 4*(col/8) + col%4, so value v of a lane of
+    // half h is key 32h + 16*beta + 4*(v/4) + v%4: a lane half holds the 32
+    // keys that its half of P.V's B operand takes, in byte order (no swaps).
     f32x16 sacc[2] = {};
     const int8_t* kb = reinterpret_cast<const int8_t*>(stg);
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
-      const int key = 32 * beta + col;
+      const int key = 32 * ((col >> 2) & 1) + 16 * beta + 4 * (col >> 3) + (col & 3);
 #pragma unroll
       for (int ks = 0; ks < D / 64; ++ks) {
         const int c0 = 4 * ks + 2 * half;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + (key * CK + (c0 ^ (key % CK))) * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + (key * CK + ((c0 + 1) ^ (key % CK))) * 16);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + (key * CK + (c0 ^ fp8_ksw<D>(key))) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + (key * CK + ((c0 + 1) ^ fp8_ksw<D>(key))) * 16);
         i32x8 kaa;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1114,31 +1139,32 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
         sacc[beta] = mfma_fp8_b16th(kaa, ql[ks], sacc[beta]);
       }
     }
-    // value i = 16*beta + v is key 32*beta + 8*(v/4) + 4*half + v%4, on page i / 8
+    // value i = 16*beta + v is key 32*half + 16*beta + 4*(v/4) + v%4
     float sv[32];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sv[16 * beta + v] = sacc[beta][v];
     if (kt >= n_full) {
-      const int lim = key_lim - kt * KT - 4 * half;
+      const int lim = key_lim - kt * KT - 32 * half;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
+        const int off = 16 * (i >> 4) + 4 * ((i & 15) >> 2) + (i & 3);
         sv[i] = off <= lim ? sv[i] : -INFINITY;
       }
     }
-    // row max over the tile: per page raw maxima times the (positive) factors
+    // row max over the tile: per block raw maxima times the (positive) factors
     // (IEEE maximum: no operand canonicalisation, and no NaN can arise here)
     auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
     float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float pm = mx(mx(sv[8 * j], sv[8 * j + 1]), sv[8 * j + 2]);
-      pm = mx(mx(pm, sv[8 * j + 3]), sv[8 * j + 4]);
-      pm = mx(mx(pm, sv[8 * j + 5]), sv[8 * j + 6]);
-      pm = mx(pm, sv[8 * j + 7]);
-      mt = mx(mt, __builtin_fmaf(pm, fac[j], madd[j]));
+    for (int beta = 0; beta < 2; ++beta) {
+      const float* w = sv + 16 * beta;
+      float pm = mx(mx(w[0], w[1]), w[2]);
+#pragma unroll
+      for (int k = 3; k < 15; k += 2) pm = mx(mx(pm, w[k]), w[k + 1]);
+      pm = mx(pm, w[15]);
+      mt = mx(mt, __builtin_fmaf(pm, fb[beta], mb[beta]));
     }
     mt = maxm_xor32(mt);
     // lazy rescale with headroom 2^2: every weight stays <= 4
@@ -1153,30 +1179,24 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       mu = m == -INFINITY ? 0.f : m;
     }
     // weights times their page's code factor, straight from the exponent
-    float off_j[4];
+    const float off_b[2] = {lb[0] - mu, lb[1] - mu};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) off_j[j] = lvs[j] - mu;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], fac[i >> 3], off_j[i >> 3]));
+    for (int i = 0; i < 32; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], fb[i >> 4], off_b[i >> 4]));
     {
       float ps[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         ps[j] = ((sv[8 * j] + sv[8 * j + 1]) + (sv[8 * j + 2] + sv[8 * j + 3])) +
                 ((sv[8 * j + 4] + sv[8 * j + 5]) + (sv[8 * j + 6] + sv[8 * j + 7]));
-      l += (ps[0] * ivs[0] + ps[1] * ivs[1]) + (ps[2] * ivs[2] + ps[3] * ivs[3]);
+      l += (ps[0] + ps[1]) * ib[0] + (ps[2] + ps[3]) * ib[1];
     }
 
-    // P^T codes as the B operand: group g takes keys 32g .. 32g+31
+    // P^T codes as the B operand: group g takes keys 32g .. 32g+31, byte t
+    // key 32g + t, which is this lane's value t
     i32x8 pb;
 #pragma unroll
-    for (int bq = 0; bq < 4; ++bq) {
-      const uint32_t d0 = fp8x4(sv[4 * bq], sv[4 * bq + 1], sv[4 * bq + 2], sv[4 * bq + 3]);
-      const uint32_t d1 = fp8x4(sv[16 + 4 * bq], sv[16 + 4 * bq + 1], sv[16 + 4 * bq + 2], sv[16 + 4 * bq + 3]);
-      const auto e = __builtin_amdgcn_permlane32_swap(d0, d1, false, false);
-      pb[2 * bq] = static_cast<int>(e[0]);
-      pb[2 * bq + 1] = static_cast<int>(e[1]);
-    }
+    for (int w = 0; w < 8; ++w)
+      pb[w] = static_cast<int>(fp8x4(sv[4 * w], sv[4 * w + 1], sv[4 * w + 2], sv[4 * w + 3]));
     // O^T += V^T . P^T: V codes of pages 2g, 2g+1 for feature d
     const int8_t* vb = reinterpret_cast<const int8_t*>(stg + Fp8Smem<D>::KB);
 #pragma unroll
