@@ -696,40 +696,52 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     // 16(i/8) + 8h + 4((i/4)%2) + i%4: each lane then holds 8 consecutive keys
     // per 16-key step, already the order of P.V's B operand (no lane swaps).
     const char* kbase = stg + krow * (D * 2);
-    bf16x8 kf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int logical = 2 * ks + half;
-      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + ((logical ^ (krow % CPR)) * 16));
-    }
-    f32x16 s = {};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-
     float sv[16];
+    auto scores = [&]() {
+      bf16x8 kf[D / 16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = s[i];
-    // one uniform branch for both masks: keys past the row's last visible key,
-    // and keys before key_begin (key_begin % 32 == 16: the first tile's first page)
-    if (kt >= n_full || kt * kKeys < a.key_begin) {
-      const int lim = key_lim - kt * kKeys - 8 * half;
-      const int lo = a.key_begin - kt * kKeys - 8 * half;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-        sv[i] = off <= lim && off >= lo ? sv[i] : -INFINITY;
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int logical = 2 * ks + half;
+        kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + ((logical ^ (krow % CPR)) * 16));
       }
-    }
-    // IEEE maximum: no operand canonicalisation (no NaN can arise here)
-    auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
-    float mt = mx(mx(sv[0], sv[1]), sv[2]);
+      f32x16 s = {};
 #pragma unroll
-    for (int i = 3; i < 15; i += 2) mt = mx(mx(mt, sv[i]), sv[i + 1]);
-    mt = mx(mt, sv[15]);
-    mt = maxm_xor32(mt);
-    const float mt_s = mt * sc;
-    if (__any(mt_s > m + 8.f)) {
+      for (int ks = 0; ks < D / 16; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = s[i];
+      // one uniform branch for both masks: keys past the row's last visible key,
+      // and keys before key_begin (key_begin % 32 == 16: the first tile's first page)
+      if (kt >= n_full || kt * kKeys < a.key_begin) {
+        const int lim = key_lim - kt * kKeys - 8 * half;
+        const int lo = a.key_begin - kt * kKeys - 8 * half;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+          sv[i] = off <= lim && off >= lo ? sv[i] : -INFINITY;
+        }
+      }
+    };
+    // weights against the running max mu, summed in four independent chains
+    auto weights = [&]() {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -mu));
+      float ps[4] = {sv[0], sv[1], sv[2], sv[3]};
+#pragma unroll
+      for (int i = 4; i < 16; ++i) ps[i & 3] += sv[i];
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    // the tile's row max (both lane halves), in exponent units
+    auto tile_max = [&]() {
+      // IEEE maximum: no operand canonicalisation (no NaN can arise here)
+      auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+      float mt = mx(mx(sv[0], sv[1]), sv[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mt = mx(mx(mt, sv[i]), sv[i + 1]);
+      mt = mx(mt, sv[15]);
+      return maxm_xor32(mt) * sc;
+    };
+    auto rescale = [&](float mt_s) {
       const float m_new = fmaxf(m, mt_s);
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
       l *= alpha;
@@ -737,14 +749,32 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
       m = m_new;
       mu = m == -INFINITY ? 0.f : m;
+    };
+    scores();
+    float lt;
+    if constexpr (D == 128) {
+      // The running max is lazy and the tile's own max is not taken unless
+      // needed: while every weight stays small against the stale max (this
+      // lane's 16 weights sum to at most 2^8, so each is at most 2^8), the
+      // sum and the accumulator are exact against it.  Otherwise (a row's
+      // first visible keys, a max that grew, an overflow) the tile is redone
+      // from the K tile still in LDS with the true max, and O and l rescaled.
+      lt = weights();
+      if (__any(!(lt <= 256.f) || m == -INFINITY)) {
+        asm volatile("" ::: "memory");  // re-read K: no registers held across
+        scores();
+        rescale(tile_max());
+        lt = weights();
+      }
+    } else {
+      // d = 64: the max first (re-reading K would hold registers that keep
+      // this kernel under 128 VGPRs, 4 waves per SIMD); rescale when a row's
+      // max grows by more than 2^8
+      const float mt_s = tile_max();
+      if (__any(mt_s > m + 8.f)) rescale(mt_s);
+      lt = weights();
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -mu));
-    // row sum in four independent chains
-    float ps[4] = {sv[0], sv[1], sv[2], sv[3]};
-#pragma unroll
-    for (int i = 4; i < 16; ++i) ps[i & 3] += sv[i];
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l += lt;
 
     // O^T += V^T . P^T, page c = keys 16c..16c+15 of the tile
     const char* vbase = stg + DmaSmem<D>::KB;
