@@ -12,7 +12,9 @@ d=128, split-KV + logsumexp merge).  Prints one JSON line:
   decode    KV GB/s of the decode calls (K+V bytes read, logical)
   roofline  of the prefill kernel (MFMA bound), roofline_decode of the decode
   cpu_baseline  the float64 oracle timed on a bounded sample on the host.
-Per-kernel times come from HIP events recorded on the stream the kernels run on.
+Per-kernel times come from HIP events recorded on the stream the kernels run on,
+created without the system-scope fence (a default event's record writes back
+the L2, which adds microseconds around the launch it brackets).
 """
 from __future__ import annotations
 
@@ -441,6 +443,53 @@ def measured_ceilings(pa, dev) -> dict:
     return res
 
 
+class FenceFreeEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, from the HIP
+    runtime torch has loaded.  Its record carries no system-scope release, so
+    it takes no L2 write-back: a default event's fence adds several
+    microseconds around the launch it brackets and slows the launch after it.
+    Elapsed times are read only after a device synchronisation."""
+
+    _hip = None
+    _FLAG = 0x20000000  # hipEventDisableSystemFence
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            path = next((l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l), None)
+            if path is None:
+                raise RuntimeError("HIP runtime not loaded (initialise torch.cuda first)")
+            cls._hip = ctypes.CDLL(path)
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(self._FLAG))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self, stream=None):
+        import torch
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        rc = self._lib().hipEventRecord(self.ev, self._ct.c_void_p(s))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end):
+        ms = self._ct.c_float()
+        rc = self._lib().hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +510,9 @@ def main():
                     help="prefill calls on fp8 pools use pa_prefill (codes widened to bf16, "
                          "products on the bf16 matrix cores) instead of pa_prefill_fp8 (Q and "
                          "P in E4M3, both products on the fp8 matrix cores)")
+    ap.add_argument("--torch-events", action="store_true",
+                    help="time the launches with torch's default events, whose record carries a "
+                         "system-scope fence (L2 write-back), instead of fence-free HIP events")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (streaming read, MFMA loops) after the timed steps")
     ap.add_argument("--one-call", action="store_true",
@@ -564,8 +616,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in launches] for _ in range(args.steps)]
+    if args.torch_events:
+        def mk():
+            return torch.cuda.Event(enable_timing=True)
+    else:
+        mk = FenceFreeEvent
+    evs = [[(mk(), mk()) for _ in launches] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -588,7 +644,9 @@ def main():
     ms_per_step = sum(per_launch_ms) if scratch is not None else wall * 1e3 / args.steps
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-              "vs_baseline": None, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)"}
+              "vs_baseline": None, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)",
+              "timing": ("torch events (system-scope fence)" if args.torch_events
+                         else "HIP events without system fence, one pair per launch")}
     parts = {}
     for (kind, wl, call, _, f8), ms, sms in zip(launches, per_launch_ms, step_ms):
         spread = {"ms_median": statistics.median(sms), "ms_min": min(sms)}
