@@ -334,16 +334,31 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.d, col, 2 * ks + half), vf[ks], dp, 0, 0, 0);
     }
     float p[16], ds[16];
+    // one wave-uniform test: every (row, key) of the tile visible to every lane
+    if (__all(key_ok & (R0 + kBT <= nrows) & (R0 >= lo_row))) {
 #pragma unroll
-    for (int bq = 0; bq < 4; ++bq) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(st.lse2 + 8 * bq + 4 * half);
-      const f32x4 dl = *reinterpret_cast<const f32x4*>(st.delta + 8 * bq + 4 * half);
+      for (int bq = 0; bq < 4; ++bq) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st.lse2 + 8 * bq + 4 * half);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(st.delta + 8 * bq + 4 * half);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = 4 * bq + r, R = R0 + 8 * bq + 4 * half + r;
-        const bool vis = key_ok & (R < nrows) & (R >= lo_row);
-        p[v] = vis ? fast_exp2(__builtin_fmaf(sv[v], sc, -l2[r])) : 0.f;
-        ds[v] = vis ? p[v] * (dp[v] - dl[r]) : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * bq + r;
+          p[v] = fast_exp2(__builtin_fmaf(sv[v], sc, -l2[r]));
+          ds[v] = p[v] * (dp[v] - dl[r]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int bq = 0; bq < 4; ++bq) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st.lse2 + 8 * bq + 4 * half);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(st.delta + 8 * bq + 4 * half);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * bq + r, R = R0 + 8 * bq + 4 * half + r;
+          const bool vis = key_ok & (R < nrows) & (R >= lo_row);
+          p[v] = vis ? fast_exp2(__builtin_fmaf(sv[v], sc, -l2[r])) : 0.f;
+          ds[v] = vis ? p[v] * (dp[v] - dl[r]) : 0.f;
+        }
       }
     }
     // dV^T += dO^T P,  dK^T += Q^T dS  (contract the 32 query rows)
@@ -494,12 +509,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.v, col, 2 * ks + half), dof[ks], dp, 0, 0, 0);
     }
     float ds[16];
+    // one wave-uniform test: every key of the tile visible to every lane's row
+    if (__all(kt * kBT + kBT - 1 <= key_lim)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kt * kBT + 8 * (v >> 2) + 4 * half + (v & 3);
-      const bool vis = key <= key_lim;
-      const float p = vis ? fast_exp2(__builtin_fmaf(sv[v], sc, -l2)) : 0.f;
-      ds[v] = vis ? p * (dp[v] - dl) : 0.f;
+      for (int v = 0; v < 16; ++v) ds[v] = fast_exp2(__builtin_fmaf(sv[v], sc, -l2)) * (dp[v] - dl);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kt * kBT + 8 * (v >> 2) + 4 * half + (v & 3);
+        const bool vis = key <= key_lim;
+        const float p = vis ? fast_exp2(__builtin_fmaf(sv[v], sc, -l2)) : 0.f;
+        ds[v] = vis ? p * (dp[v] - dl) : 0.f;
+      }
     }
     // dQ^T += K^T dS^T  (contract the 32 keys)
 #pragma unroll
