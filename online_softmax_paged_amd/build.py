@@ -22,8 +22,10 @@ SOURCES = ["api.hip", "kv_cache.hip", "decode.hip", "prefill.hip", "backward.hip
            "allocator.cpp"]
 
 # Keep MFMA accumulators in ordinary VGPRs so the softmax can rescale them
-# without copies to and from the accumulation registers.
-PER_FILE = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# (and the backward read its score blocks) without copies to and from the
+# accumulation registers.
+PER_FILE = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
