@@ -230,10 +230,17 @@ struct RowsStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
   constexpr int NI = kBT * D * 2 / 1024;  // 1 KiB loads per operand tile
-  __shared__ RowsStage<D> sm[2];
+  // d = 128: one stage of query tiles, and V of the workgroup's 128 keys in
+  // LDS, each lane keeping its own key's operands there (written and read by
+  // that lane only), which leaves the registers for two waves per SIMD.
+  // d = 64 fits two waves with V in registers and two stages.
+  constexpr bool kVL = D == 128;
+  constexpr int NS = kVL ? 1 : 2;
+  __shared__ RowsStage<D> sm[NS];
+  __shared__ uint16_t vsm[kVL ? 4 * kBT * D : 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -252,7 +259,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   // this lane's key (its MFMA column) and the operands of the wave's keys
   const int key = k0 + 32 * wave + col;
   const int32_t phys = page_id(a, b, key / kPage, n_pages);
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16], vf[kVL ? 1 : D / 16];
+  uint16_t* const vw = vsm + (kVL ? wave * (kBT * D) : 0);  // this wave's keys, row-tile layout
   {
     const int64_t base = (static_cast<int64_t>(phys < 0 ? 0 : phys) * Hkv + g) * (kPage * D) +
                          (key % kPage) * D + half * 8;
@@ -261,7 +269,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(a.k + base + ks * 16);
       bf16x8 y = *reinterpret_cast<const bf16x8*>(a.vtm + base + ks * 16);
       kf[ks] = phys < 0 ? bf16x8{} : x;
-      vf[ks] = phys < 0 ? bf16x8{} : y;
+      if constexpr (kVL)
+        *reinterpret_cast<bf16x8*>(vw + row_pos<D>(col, 2 * ks + half)) = phys < 0 ? bf16x8{} : y;
+      else
+        vf[ks] = phys < 0 ? bf16x8{} : y;
     }
   }
   f32x16 dk[D / 32], dv[D / 32];
@@ -314,16 +325,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   // pair then read the same tiles at about the same time
   const int t_first = a.causal ? max(0, k0 - pos_base) : 0;
   const int tile0 = (t_first * G) / kBT, n_tiles = (nrows + kBT - 1) / kBT;
-  if (tile0 < n_tiles) stage_tile(n_tiles - 1, 0);
-  wait_vmcnt<0>();
   // a query row R (token R / G) sees this lane's key when R >= lo_row
   const int lo_row = a.causal ? (key - pos_base) * G : INT_MIN;
   const bool key_ok = key < ctx;
+  if (!kVL && tile0 < n_tiles) stage_tile(n_tiles - 1, 0);
+  wait_vmcnt<0>();
   for (int it = n_tiles - 1; it >= tile0; --it) {
     const int R0 = it * kBT;
-    const int s = (n_tiles - 1 - it) & 1;
-    __syncthreads();  // tile it has landed; the stage of the tile before is free
-    if (it > tile0) stage_tile(it - 1, s ^ 1);
+    int s = 0;
+    if constexpr (kVL) {
+      __syncthreads();  // every wave is done with the tile before
+      stage_tile(it, 0);
+      wait_vmcnt<0>();
+      __syncthreads();  // tile it has landed
+    } else {
+      s = (n_tiles - 1 - it) & 1;
+      __syncthreads();  // tile it has landed; the stage of the tile before is free
+      if (it > tile0) stage_tile(it - 1, s ^ 1);
+    }
     const RowsStage<D>& st = sm[s];
 
     // S and dP for (query rows x this lane's key)
@@ -331,7 +350,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.q, col, 2 * ks + half), kf[ks], sv, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.d, col, 2 * ks + half), vf[ks], dp, 0, 0, 0);
+      bf16x8 vk;
+      if constexpr (kVL)
+        vk = row_read<D>(vw, col, 2 * ks + half);
+      else
+        vk = vf[ks];
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<D>(st.d, col, 2 * ks + half), vk, dp, 0, 0, 0);
     }
     float p[16], ds[16];
     // one wave-uniform test: every (row, key) of the tile visible to every lane
@@ -372,7 +396,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(st.qt, d, c, half), sb, dk[db], 0, 0, 0);
       }
     }
-    wait_vmcnt<0>();  // this wave's loads of the next tile are in LDS
+    if constexpr (!kVL) wait_vmcnt<0>();  // this wave's loads of the next tile are in LDS
   }
 
   // write this lane's key: dK token-major, dV feature-major (the pool's layouts)
