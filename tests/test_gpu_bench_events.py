@@ -1,0 +1,36 @@
+"""bench.py times each launch with HIP events created without the system-scope
+fence.  They must measure the work between them as torch's default events do:
+ten 256 MiB device copies take the same time under both (within 15%), and no
+less than the copies' bytes allow at the HBM peak."""
+import pytest
+import torch
+
+import bench
+
+pytestmark = pytest.mark.gpu
+
+
+def _copies_ms(make_event, x, y, reps=10):
+    e0, e1 = make_event(), make_event()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def test_fence_free_events_time_like_torch_events():
+    x = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    ff = [_copies_ms(bench.FenceFreeEvent, x, y) for _ in range(3)]
+    tt = [_copies_ms(lambda: torch.cuda.Event(enable_timing=True), x, y) for _ in range(3)]
+    f, t = min(ff), min(tt)
+    print(f"fence-free {f:.3f} ms, torch events {t:.3f} ms", flush=True)
+    # 10 copies read and write 256 MiB each: at 8 TB/s no less than 0.67 ms
+    floor_ms = 10 * 2 * (256 << 20) / 8e12 * 1e3
+    assert f >= floor_ms and t >= floor_ms
+    assert 0.85 <= f / t <= 1.15
