@@ -408,8 +408,8 @@ pa_status pa_plan_append(pa_allocator* a, int32_t* block_table, int32_t bt_strid
 /* ------------------------------------------------------------ measurement probes
  * Not part of the attention path.  Two kernels that measure what this GPU
  * sustains, so that each attention kernel's rate can be read against a
- * measured ceiling as well as the spec peak (the survey's measurement section
- * asks for both; bench.py runs these beside the attention kernels).
+ * measured ceiling as well as the spec peak (bench.py runs these beside the
+ * attention kernels).
  *
  * pa_probe_stream_read: every 16-byte word of buf (device memory, bytes a
  *   multiple of 16) is read once with non-temporal loads by `blocks`
