@@ -152,8 +152,12 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
 /* ------------------------------------------------------------------ gather
  * Copy each sequence's logical tokens out of the pool, through its block
  * table, into contiguous token-major buffers (bit-exact copy of the stored
- * bytes; fp8 codes are copied without scaling).  Used to check the pool and
- * block-table addressing and as a bandwidth probe.
+ * bytes; fp8 codes are copied without scaling).  This is the lookup step of
+ * the paged loop in the "core modules" chapter page, section 2.2 (logical
+ * block j of a sequence -> physical block block_table[j] -> its K and V), and
+ * of the block-table mapping in the survey page, section 3, "core
+ * principle", done on its own.  Used to check the pool and block-table
+ * addressing and as a bandwidth probe.
  *   block_table : int32 [num_seqs, bt_stride] (device)
  *   ctx_lens    : int32 [num_seqs] (device)
  *   cu_ctx      : int32 [num_seqs + 1] (device), prefix sums of ctx_lens
@@ -166,7 +170,12 @@ pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32
 
 /* ------------------------------------------------------------------ prefill
  * Causal (or full) attention of a batch of query chunks against the paged
- * cache.  Sequence b has q_len_b = cu_q_lens[b+1] - cu_q_lens[b] query tokens
+ * cache: softmax(scale Q K^T) V (survey page, section 1) computed tile by tile
+ * with a running max, a running exp-sum and a rescaled accumulator, only the
+ * logsumexp kept (survey page, section 2, "core principle" and
+ * FlashAttention-2 improvements; "core modules" chapter, section 2.1), the
+ * K/V tiles found page by page through the block table (the paged loop of
+ * the "core modules" chapter, section 2.2).  Sequence b has q_len_b = cu_q_lens[b+1] - cu_q_lens[b] query tokens
  * that are the LAST q_len_b of its ctx_len_b cached tokens (their K/V must
  * already be in the pool): query i of sequence b sits at position
  * ctx_len_b - q_len_b + i and, when causal, sees keys 0..that position.
@@ -181,6 +190,8 @@ pa_status pa_gather_kv(const pa_kv_pool* pool, const int32_t* block_table, int32
  * fp8 pool.  head_dim 64 or 128; num_q_heads / num_kv_heads in {1,2,4,8,16}.
  * q and o must be 16-byte aligned.  A sequence with q_len_b = 1 is a decode
  * row, so one call can serve a mixed batch of chunked prefills and decodes.
+ * A row that sees no key (only possible when the device-resident contract is
+ * broken: ctx_len_b = 0 or q_len_b > ctx_len_b) gets O = 0 and LSE = -inf.
  * Key splits: each query tile's visible keys can be cut into num_splits
  * contiguous ranges of 32-key tiles; each range gives a normalised partial
  * output and logsumexp in the workspace, and a second pass merges them by
@@ -290,7 +301,9 @@ pa_status pa_prefill_backward(const pa_kv_pool* pool, const void* q, const void*
  *                  max_ctx_len (checked).
  *   num_q_tokens : cu_q_lens[num_seqs], the rows of q and o; 1 <= num_q_tokens
  *                  <= num_seqs * max_q_len (checked).  Rows of a sequence past
- *                  num_q_tokens are not written.
+ *                  num_q_tokens are not written.  When max_q_len is 1 every
+ *                  sequence has exactly one query (q_len_b >= 1 as for every
+ *                  call), so num_q_tokens must equal num_seqs (checked).
  *   prefix_splits, suffix_splits : key splits of passes 1 and 2, 0 = choose
  *                  with pa_shared_prefix_num_splits(), at most 64 each.
  *   workspace    : at least pa_shared_prefix_workspace_bytes(num_q_tokens,
@@ -347,6 +360,12 @@ pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dty
  *   the longest sequence is over 3 times the mean, else pa_decode_num_splits.
  */
 #define PA_DECODE_BALANCED (-1)
+/* Workspace of pa_decode with num_splits > 1: one normalised fp32 partial
+ * output row of head_dim floats and one fp32 logsumexp per (sequence, query
+ * head, split), the state each split keeps before the merge (the partial
+ * softmax statistics of the "core modules" chapter, section 2.1; the survey
+ * page, section 2, "core principle", keeps the same max/sum pair per block).
+ * Independent of the context lengths; 0 when num_splits <= 1. */
 size_t pa_decode_balanced_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t max_ctx_len);

@@ -308,6 +308,9 @@ pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dty
     return PA_ERR_INVALID_ARG;
   if (prefix_splits < 0 || prefix_splits > 64 || suffix_splits < 0 || suffix_splits > 64)
     return PA_ERR_INVALID_ARG;
+  // With one query per sequence the suffix pass is the decode kernel, which
+  // takes query row b as sequence b's query: the rows must be one per sequence.
+  if (max_q_len == 1 && num_q_tokens != num_seqs) return PA_ERR_INVALID_ARG;
   int32_t auto_p = 1, auto_s = 1;
   s = pa_shared_prefix_num_splits(num_seqs, pool->num_kv_heads, num_q_heads, max_q_len,
                                   max_ctx_len, prefix_len, num_q_tokens, &auto_p, &auto_s);

@@ -278,8 +278,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   if (t0 >= qlen) return;
   const int pos_base = ctx - qlen;            // position of query token 0
   const int t_last = min(t0 + TQ, qlen) - 1;  // last token of this tile
-  const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
-  if (kmax <= 0) return;                      // inconsistent lengths: nothing visible
+  // Inconsistent lengths (ctx = 0, or q_len > ctx) leave some or all rows
+  // nothing to see: those rows still get O = 0 and LSE = -inf (or an empty
+  // partial) from the epilogue, with no key tile visited.
+  const int kmax = max(0, a.causal ? min(ctx, pos_base + t_last + 1) : ctx);
   const int n_kt_all = (kmax + kKeys - 1) / kKeys;
   // this split's key tiles [kt_begin, n_kt), from the tile holding key_begin
   const int kt_first = a.key_begin / kKeys;
@@ -583,8 +585,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
   if (t0 >= qlen) return;
   const int pos_base = ctx - qlen;
   const int t_last = min(t0 + TQ, qlen) - 1;
-  const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
-  if (kmax <= 0) return;
+  const int kmax = max(0, a.causal ? min(ctx, pos_base + t_last + 1) : ctx);  // 0: rows left empty
   const int n_kt_all = (kmax + kKeys - 1) / kKeys;
   // this split's key tiles [kt_begin, n_kt), from the tile holding key_begin
   const int kt_first = a.key_begin / kKeys;
@@ -942,8 +943,7 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
   if (t0 >= qlen) return;
   const int pos_base = ctx - qlen;
   const int t_last = min(t0 + TQ, qlen) - 1;
-  const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
-  if (kmax <= 0) return;
+  const int kmax = max(0, a.causal ? min(ctx, pos_base + t_last + 1) : ctx);  // 0: rows left empty
   const int n_kt_all = (kmax + KT - 1) / KT;
   const int per_split = (n_kt_all + S - 1) / S;
   const int kt_begin = split * per_split;

@@ -196,6 +196,9 @@ def test_shared_prefix_checks():
                 dict(max_q=0)):
         assert _shared(p, **bad) == pa.PA_ERR_INVALID_ARG, bad
     assert _shared(p, B=0) == pa.PA_OK
+    # one query per sequence: the decode suffix pass takes row b as sequence b
+    assert _shared(p, max_q=1, T=1) == pa.PA_ERR_INVALID_ARG
+    assert _shared(p, max_q=1, T=2) == pa.PA_ERR_WORKSPACE        # rows == sequences: accepted
     # split choice: the packed prefix pass has few query tiles, so its keys split
     sp, ss = pa.shared_prefix_num_splits(8, 8, 32, 1, 32768, 32768 - 64, 8)
     assert sp > 1 and ss == 1

@@ -191,3 +191,91 @@ def test_append_error_bound():
     # each re-encoding adds at most half a code step at the top of the range
     # (16 code units of the scale at that time); four rounds at most
     assert np.abs(got - ref).max() <= 4 * 16 * amax / 448
+
+
+# ---------------------------------------------------------------- copy-on-write pins
+# The copy a sequence takes before writing into a block it shares (survey page,
+# section 3, core principle: shared blocks carry reference counts and are copied
+# before a sharer changes them).  What the copy must achieve is fixed without
+# looking at oracle.pool.copy_blocks: the destination then holds what the source
+# held (all heads, K, V and both fp8 scales), nothing else changes, and
+# attention through the copy equals attention through the original.
+def _filled_pool(kv_dtype, nb=8, hkv=2, d=8, seed=11):
+    g = torch.Generator().manual_seed(seed)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16}[kv_dtype]
+    p = OraclePool(nb, hkv, d, kv_dtype)
+    # every page written whole, each with its own value range (so its own fp8 scales)
+    for page in range(nb):
+        mag = 0.25 * (page + 1)
+        k = (torch.randn(16, hkv, d, generator=g) * mag).to(dt)
+        v = (torch.randn(16, hkv, d, generator=g) * (2.0 - 0.2 * page)).to(dt)
+        write_kv(p, k, v, torch.arange(page * 16, page * 16 + 16, dtype=torch.int32))
+    return p
+
+
+def _snapshot(p):
+    s = [p.k.copy(), p.v.copy()]
+    if p.kv_dtype == "fp8":
+        s += [p.k_scale.copy(), p.v_scale.copy()]
+    return s
+
+
+def _copy_pins_hold(kv_dtype, copy_fn):
+    """True when copy_fn(pool, src, dst) passes every pin of a block copy."""
+    p = _filled_pool(kv_dtype)
+    src, dst = [1, 5, 0], [6, 2, 7]
+    before = _snapshot(p)
+    copy_fn(p, src, dst)
+    after = _snapshot(p)
+    for b_arr, a_arr in zip(before, after):
+        for s, d in zip(src, dst):
+            if not np.array_equal(a_arr[d], b_arr[s], equal_nan=True):   # byte for byte
+                return False
+        others = [i for i in range(p.num_blocks) if i not in dst]
+        if not np.array_equal(a_arr[others], b_arr[others], equal_nan=True):
+            return False
+    # attention through a table that names the copies equals the same table on
+    # the originals, for a query per sequence over 3 pages
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn(2, 4, p.head_dim, generator=g, dtype=torch.float64)
+    t_src = torch.tensor([[1, 5, 0], [0, 1, 5]], dtype=torch.int32)
+    t_dst = torch.tensor([[6, 2, 7], [7, 6, 2]], dtype=torch.int32)
+    cu, ctx = torch.tensor([0, 1, 2]), torch.tensor([45, 48])
+    o1, l1 = oracle.paged_attention(p, q, cu, ctx, t_src, 4, 0.3, True)
+    o2, l2 = oracle.paged_attention(p, q, cu, ctx, t_dst, 4, 0.3, True)
+    return np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+def test_copy_blocks_pins(kv_dtype):
+    assert _copy_pins_hold(kv_dtype, oracle.pool.copy_blocks)
+
+
+def test_copy_pins_catch_planted_mistakes():
+    """Plausible mistakes in a block copy each fail a pin above: fp8 scales not
+    copied, only K copied, only the first KV head copied, source and
+    destination swapped."""
+    def no_scales(p, src, dst):
+        for s, d in zip(src, dst):
+            p.k[d], p.v[d] = p.k[s], p.v[s]
+
+    def only_k(p, src, dst):
+        for s, d in zip(src, dst):
+            p.k[d] = p.k[s]
+            if p.kv_dtype == "fp8":
+                p.k_scale[d], p.v_scale[d] = p.k_scale[s], p.v_scale[s]
+
+    def first_head(p, src, dst):
+        for s, d in zip(src, dst):
+            p.k[d, 0], p.v[d, 0] = p.k[s, 0], p.v[s, 0]
+            if p.kv_dtype == "fp8":
+                p.k_scale[d], p.v_scale[d] = p.k_scale[s], p.v_scale[s]
+
+    def swapped(p, src, dst):
+        oracle.pool.copy_blocks(p, dst, src)
+
+    assert not _copy_pins_hold("fp8", no_scales)
+    for kv in ("bf16", "fp8"):
+        assert not _copy_pins_hold(kv, only_k)
+        assert not _copy_pins_hold(kv, first_head)
+        assert not _copy_pins_hold(kv, swapped)

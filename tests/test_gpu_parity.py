@@ -503,15 +503,58 @@ def test_named_workload_full(k):
         _check_call(wl, call, pool, opool)
 
 
-def test_named_prefill_4x4096_sampled():
-    """Full-size causal prefill in the benchmark's launch configuration; the
-    oracle checks sampled rows one by one."""
-    _log("named workload 3 (sampled rows)")
+def test_named_prefill_4x4096_every_row():
+    """Full-size causal prefill (4 x 4096 tokens, 32 query / 8 KV heads, d 128)
+    in the benchmark's launch configuration, every (token, head) row against
+    the oracle.  o starts as NaN and lse as +inf, so a query tile the kernel
+    never wrote fails, and one written with another tile's rows fails on its
+    values."""
+    _log("named workload 3 (every row)")
     wl, opool = _named(3)
     pool = H.device_pool(wl)
     call = wl.calls[0]
-    rows = H.sample_rows(call, wl.num_q_heads, 96, seed=3)
-    _check_call(wl, call, pool, opool, rows=rows)
+    dc = H.DeviceCall(wl, call)
+    T, Hq, _ = dc.q.shape
+    o = torch.full_like(dc.q, float("nan"))
+    lse = torch.full((T, Hq), float("inf"), dtype=torch.float32, device=dc.q.device)
+    S = pa.prefill_num_splits(len(call.q_lens), wl.num_kv_heads, Hq, dc.max_q_len, dc.max_ctx_len)
+    dc.run(pool, num_splits=S, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), "unwritten rows"
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    _log(f"  every row: max|dO|={eo:.3e} max|dLSE|={el:.3e} tol={H.TOL['bf16']}")
+    assert eo <= H.TOL["bf16"] and el <= H.TOL["bf16"], (eo, el)
+
+
+@pytest.mark.parametrize("kv,ctx0,splits,fp8p", [
+    ("bf16", 0, 1, False), ("bf16", 0, 3, False), ("bf16", 5, 1, False),
+    ("fp8", 5, 2, False), ("fp8", 0, 1, True), ("fp8", 0, 3, True)])
+def test_rows_that_see_no_key_are_empty(kv, ctx0, splits, fp8p):
+    """Lengths outside the contract (a sequence with ctx 0, or more queries
+    than cached tokens) leave rows with no visible key: every such row, also
+    with key splits, comes out as O = 0 and LSE = -inf, and the other rows as
+    the oracle has them.  o and lse start as NaN and +inf."""
+    _log(f"empty rows {kv} ctx0={ctx0} splits={splits} fp8_products={fp8p}")
+    wl = workloads.small("prefill", kv_dtype=kv, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         ctx_lens=(40, 300), q_lens=(8, 100), seed=71)
+    call = wl.calls[0]
+    call.ctx_lens = call.ctx_lens.clone()
+    call.ctx_lens[0] = ctx0          # sequence 0: 8 queries over ctx0 keys
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    dc = H.DeviceCall(wl, call)
+    T, Hq, _ = dc.q.shape
+    o = torch.full_like(dc.q, float("nan"))
+    lse = torch.full((T, Hq), float("inf"), dtype=torch.float32, device=dc.q.device)
+    dc.run(pool, num_splits=splits, out=o, lse=lse, fp8_products=fp8p)
+    torch.cuda.synchronize()
+    empty = 8 - ctx0                 # sequence 0's rows before position 0
+    assert bool((o[:empty] == 0).all()) and bool((lse[:empty] == -float("inf")).all())
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    tol = H.tolerance(wl)
+    _log(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e} tol={tol}")
+    assert eo <= tol and el <= tol
 
 
 # ------------------------------------------------------------ invariants
