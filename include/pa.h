@@ -38,7 +38,8 @@
  *    so bt_stride >= ceil(max_ctx_len / 16) (checked).  A block id outside
  *    [0, num_blocks) is never dereferenced (the page is treated as empty), but
  *    the result is then unspecified.
- *  - Calls are reentrant; the library keeps no mutable global state.
+ *  - Calls are reentrant; the library keeps no mutable global state (except
+ *    pa_decode_noalloc's fixed device array, see there).
  */
 #ifndef PA_H
 #define PA_H
@@ -379,6 +380,34 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, voi
                     int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
                     int32_t max_ctx_len, float scale, int32_t num_splits, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------ decode without allocation
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation, kernels and results as pa_decode with the
+ * same num_splits (bit for bit), but the split partials go to a fixed device
+ * array of PA_SCRATCH_BYTES inside the library instead of a workspace.  Calls
+ * no hipMalloc, hipFree or other allocating routine.
+ *   - Each GPU the library runs on holds its own copy of the array until the
+ *     process ends; its address is looked up on the first call on that GPU.
+ *     The current device (hipGetDevice) must be the one `stream` and all
+ *     buffers belong to.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams, other threads) race and must not be
+ *     issued.  Stream-ordered calls on one stream are fine.
+ *   - The array keeps the last call's partials; no call needs it cleared.
+ * Arguments as pa_decode without the workspace.  Errors as pa_decode, plus
+ * PA_ERR_WORKSPACE (before anything is enqueued) when the partials of the
+ * chosen split count would need more than PA_SCRATCH_BYTES
+ * (pa_decode_workspace_bytes, or pa_decode_balanced_workspace_bytes for
+ * PA_DECODE_BALANCED).  Breaks the "no mutable global state" convention above
+ * only through that array.
+ */
+#define PA_SCRATCH_BYTES (8u << 20)
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                            float* lse, const int32_t* ctx_lens, const int32_t* block_table,
+                            int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_ctx_len, float scale, int32_t num_splits, void* stream);
 
 /* ------------------------------------------------------------------ blocks
  * Host-side block allocator for a pool of num_blocks physical blocks: a free

@@ -76,6 +76,9 @@ _dec_bal_ws = _sig("pa_decode_balanced_workspace_bytes", _SZ, [_I32, _I32, _I32,
 _decode = _sig("pa_decode", ctypes.c_int,
                [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F, _I32,
                 _VP, _SZ, _VP])
+_decode_noalloc = _sig("pa_decode_noalloc", ctypes.c_int,
+                      [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F,
+                       _I32, _VP])
 _alloc_create = _sig("pa_allocator_create", _VP, [_I32])
 _alloc_destroy = _sig("pa_allocator_destroy", None, [_VP])
 _alloc_block = _sig("pa_alloc_block", _I32, [_VP])
@@ -99,7 +102,9 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
             "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits",
             "pa_backward_workspace_bytes", "pa_prefill_backward", "pa_prefill_fp8",
-            "pa_probe_stream_read", "pa_probe_mfma"]
+            "pa_probe_stream_read", "pa_probe_mfma", "pa_decode_noalloc"]
+
+SCRATCH_BYTES = 8 << 20   # PA_SCRATCH_BYTES
 
 DECODE_BALANCED = -1
 
@@ -466,6 +471,20 @@ def decode(pool: KVPool, q: torch.Tensor, ctx_lens, block_table, scale: float,
                    num_splits, _ptr(workspace), 0 if workspace is None else workspace.numel(),
                    _stream(stream)), "pa_decode")
     return o, lse
+
+
+def decode_noalloc(pool: KVPool, q: torch.Tensor, ctx_lens, block_table, scale: float,
+                   max_ctx_len: int, out: torch.Tensor, lse: torch.Tensor, num_splits: int = 0,
+                   stream=None):
+    """pa_decode_noalloc: pa_decode with the split partials in the library's
+    fixed per-device array, for callers that cannot allocate.  Allocates
+    nothing here either: out and lse are the caller's.  Calls that may overlap
+    on one GPU race (they share the array)."""
+    B, Hq, _ = q.shape
+    _check(_decode_noalloc(pool.c, _ptr(q), _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(ctx_lens),
+                           _ptr(block_table), block_table.shape[1], B, Hq, max_ctx_len, scale,
+                           num_splits, _stream(stream)), "pa_decode_noalloc")
+    return out, lse
 
 
 class BlockAllocator:

@@ -3,6 +3,9 @@
 // failed check.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pa_internal.h"
 
 using namespace pa;
@@ -495,6 +498,70 @@ pa_status pa_decode(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, voi
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   }
   return launched(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------- decode without allocation
+// pa_decode_noalloc keeps the split partials in this fixed device array instead
+// of a caller's workspace.  Each GPU the library runs on holds its own copy
+// (PA_SCRATCH_BYTES) until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device array: its device address is looked up
+// once per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[PA_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on its first use).
+pa_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return PA_ERR_LAUNCH;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype, void* o,
+                            float* lse, const int32_t* ctx_lens, const int32_t* block_table,
+                            int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_ctx_len, float scale, int32_t num_splits, void* stream) {
+  if (num_seqs == 0 && pool) return check_pool(pool);
+  pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
+                           num_q_heads, max_ctx_len, scale);
+  if (s != PA_OK) return s;
+  if (num_splits < PA_DECODE_BALANCED || num_splits > 256) return PA_ERR_INVALID_ARG;
+  if (num_splits == 0) num_splits = pa_decode_num_splits(num_seqs, pool->num_kv_heads, max_ctx_len);
+  const size_t need =
+      num_splits == PA_DECODE_BALANCED
+          ? balanced_ws_bytes(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                              max_ctx_len, 0)
+          : pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim, num_splits);
+  if (need > PA_SCRATCH_BYTES) return PA_ERR_WORKSPACE;  // beyond the fixed array
+  void* ws = nullptr;
+  if (need > 0) {
+    s = device_scratch(&ws);
+    if (s != PA_OK) return s;
+  }
+  return pa_decode(pool, q, q_dtype, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
+                   num_q_heads, max_ctx_len, scale, num_splits, ws, need, stream);
 }
 
 }  // extern "C"

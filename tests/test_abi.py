@@ -295,3 +295,22 @@ def test_write_kv_checks():
     f = _FakePool(kv_dtype=pa.PA_FP8_E4M3)
     assert pa._write_ws(f.c) == 3 * 4 * 8
     assert pa._write(f.c, 0x1000, 0x2000, pa.PA_BF16, 0x3000, 4, None, 0, None) == pa.PA_ERR_WORKSPACE
+
+
+def test_decode_noalloc_checks():
+    """Refusals come from host checks before the device array is looked up
+    (no GPU needed)."""
+    def call(**kw):
+        a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, ctx=0x9000, bt=0xa000,
+                 stride=2048, B=64, Hq=64, max_ctx=32768, scale=0.1, splits=256)
+        a.update(kw)
+        return pa._decode_noalloc(_FakePool(num_kv_heads=8).c, a["q"], a["q_dtype"], a["o"],
+                                  a["lse"], a["ctx"], a["bt"], a["stride"], a["B"], a["Hq"],
+                                  a["max_ctx"], a["scale"], a["splits"], None)
+    assert pa.decode_workspace_bytes(64, 64, 128, 256) > pa.SCRATCH_BYTES
+    assert call() == pa.PA_ERR_WORKSPACE                  # partials past the fixed array
+    assert call(splits=257) == pa.PA_ERR_INVALID_ARG
+    assert call(splits=-2) == pa.PA_ERR_INVALID_ARG
+    assert call(q=0) == pa.PA_ERR_INVALID_ARG
+    assert call(stride=3) == pa.PA_ERR_INVALID_ARG
+    assert call(B=0) == pa.PA_OK
