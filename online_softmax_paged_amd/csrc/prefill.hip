@@ -1090,7 +1090,12 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       sel[4 + k] = w1;
     }
   }
-  float m = -INFINITY, l = 0.f, lq = 0.f, mu = 0.f;  // lq: sum of the rounded weights
+  float m = -INFINITY, lq = 0.f, mu = 0.f;  // lq: sum of the rounded weights
+  // Rows that see fewer than 64 keys see them all in key tile 0, where P is
+  // rounded in two E4M3 parts (the second through the block scale 2^-4): one
+  // part alone moves such a row by up to 1/15 of its V spread; rows that see
+  // more average the rounding down.
+  const bool short_rows = (a.causal ? first_pos + 1 : ctx) < 64;
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -1136,12 +1141,11 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
       madd[j] = lvs[j] == -INFINITY ? -INFINITY : 0.f;
     }
     // this lane's scores of block beta all lie on page 2*half + beta
-    float fb[2], lb[2], ib[2], mb[2];
+    float fb[2], lb[2], mb[2];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
       fb[beta] = half ? fac[2 + beta] : fac[beta];
       lb[beta] = half ? lvs[2 + beta] : lvs[beta];
-      ib[beta] = half ? ivs[2 + beta] : ivs[beta];
       mb[beta] = half ? madd[2 + beta] : madd[beta];
     }
 
@@ -1201,7 +1205,6 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     if (__any(mt > m + 2.f)) {
       const float m_new = fmaxf(m, mt);
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
-      l *= alpha;
       lq *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
@@ -1212,14 +1215,6 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     const float off_b[2] = {lb[0] - mu, lb[1] - mu};
 #pragma unroll
     for (int i = 0; i < 32; ++i) sv[i] = fast_exp2(__builtin_fmaf(sv[i], fb[i >> 4], off_b[i >> 4]));
-    {
-      float ps[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ps[j] = ((sv[8 * j] + sv[8 * j + 1]) + (sv[8 * j + 2] + sv[8 * j + 3])) +
-                ((sv[8 * j + 4] + sv[8 * j + 5]) + (sv[8 * j + 6] + sv[8 * j + 7]));
-      l += (ps[0] + ps[1]) * ib[0] + (ps[2] + ps[3]) * ib[1];
-    }
 
     // P^T codes as the B operand: group g takes keys 32g .. 32g+31, byte t
     // key 32g + t, which is this lane's value t
@@ -1244,24 +1239,46 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     }
     // rounded weights: rows 0..3 (values 0..3 of group 0's lanes) are the page
     // sums of the codes; group 1's lanes hold rows 4..7, which are zero
-    {
-      const f32x16 qs = mfma_fp8(sel, pb, f32x16{});
-      lq += (qs[0] * ivs[0] + qs[1] * ivs[1]) + (qs[2] * ivs[2] + qs[3] * ivs[3]);
+    f32x16 qs = mfma_fp8(sel, pb, f32x16{});
+    if (kt == 0 && short_rows) {  // uniform: P's second E4M3 part, 16 x the remainder
+      i32x8 pl;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t h = static_cast<uint32_t>(pb[w]);
+        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(h), false);
+        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(h), true);
+        pl[w] = static_cast<int>(fp8x4(16.f * (sv[4 * w] - d01[0]), 16.f * (sv[4 * w + 1] - d01[1]),
+                                       16.f * (sv[4 * w + 2] - d23[0]), 16.f * (sv[4 * w + 3] - d23[1])));
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = db * 32 + col;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (2 * half) * (kPage * D) + d * kPage);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (2 * half + 1) * (kPage * D) + d * kPage);
+        i32x8 va;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          va[k] = static_cast<int>(lo[k]);
+          va[4 + k] = static_cast<int>(hi[k]);
+        }
+        acc[db] = mfma_fp8_b16th(va, pl, acc[db]);
+      }
+      qs = mfma_fp8_b16th(sel, pl, qs);
     }
+    lq += (qs[0] * ivs[0] + qs[1] * ivs[1]) + (qs[2] * ivs[2] + qs[3] * ivs[3]);
     if (kt + 2 < n_kt) wait_vmcnt<NI>(); else wait_vmcnt<0>();
     __syncthreads();
   }
 
   wait_vmcnt<0>();
-  l = sum_xor32(l);
   lq = sum_xor32(lq);
   if (!row_ok) return;
-  // acc holds codes: times sv_max / 112 it is sum(w V); write_rows divides
-  // by l, so fold l / lq in to divide by the rounded weights' sum instead
-  const float back = sv_max * (1.f / 112.f) * (lq > 0.f ? l / lq : 0.f);
+  // acc holds codes: times sv_max / 112 it is sum(w V); write_rows divides by
+  // the rounded weights' sum, which also gives the logsumexp
+  const float back = sv_max * (1.f / 112.f);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] *= back;
-  write_rows<D>(a, acc, m, l, qrow, split, half);
+  write_rows<D>(a, acc, m, lq, qrow, split, half);
 }
 
 // Merge of the key splits of every query row: the logsumexp-weighted sum of
