@@ -31,7 +31,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
-PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 1 MI355X"
 
@@ -313,15 +312,14 @@ def bench_shared_prefix_decode(args):
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     S = pa.decode_choose_splits(B, wl.num_kv_heads, mc, int(call.ctx_lens.sum()))
     ws = torch.empty(max(1, pa.decode_workspace_bytes(B, Hq, D, S)), dtype=torch.uint8, device=dev)
-    sp, ss = pa.shared_prefix_num_splits(B, wl.num_kv_heads, Hq, 1, mc, P, B)
-    ws2 = torch.empty(pa.shared_prefix_workspace_bytes(B, Hq, D, sp + ss), dtype=torch.uint8,
-                      device=dev)
+    plan = pa.shared_prefix_plan(pool, B, Hq, 1, mc, P, B)
+    ws2 = torch.empty(max(1, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
     fns = {
         "decode": lambda: pa.decode(pool, q, ctx, bt, wl.scale, max_ctx_len=mc, num_splits=S,
                                     workspace=ws, out=o, lse=lse),
         "shared_prefix": lambda: pa.prefill_shared_prefix(
             pool, q, cu, ctx, bt, wl.scale, P, max_q_len=1, max_ctx_len=mc, out=o, lse=lse,
-            prefix_splits=sp, suffix_splits=ss, workspace=ws2),
+            workspace=ws2),
     }
     scratch = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
     logical = decode_kv_bytes(call, wl)
@@ -350,7 +348,8 @@ def bench_shared_prefix_decode(args):
               "parts": {"decode_ms": times["decode"], "shared_prefix_ms": ms,
                         "speedup": times["decode"] / ms, "logical_kv_bytes": logical,
                         "unique_kv_bytes": unique, "decode_splits": S,
-                        "shared_prefix_splits": [sp, ss],
+                        "shared_prefix_plan": {k: plan[k] for k in (
+                            "mode", "prefix_splits", "suffix_splits", "plain_splits")},
                         "unique_gbps": unique / (ms * 1e-3) / 1e9}}
     print(json.dumps(result), flush=True)
 
@@ -372,19 +371,30 @@ def one_call_timings(pa, wl, pool, dev, args, scratch):
     S = pa.prefill_num_splits(B, wl.num_kv_heads, Hq, mq, mc)
     ws = torch.empty(max(1, pa.prefill_workspace_bytes(B, mq, Hq, D, S)), dtype=torch.uint8,
                      device=dev)
-    sp, ss = pa.shared_prefix_num_splits(B, wl.num_kv_heads, Hq, mq, mc, wl.shared_prefix, T)
-    ws2 = torch.empty(pa.shared_prefix_workspace_bytes(T, Hq, D, sp + ss), dtype=torch.uint8,
-                      device=dev)
+    plans = {m: pa.shared_prefix_plan(pool, B, Hq, mq, mc, wl.shared_prefix, T, mode=m)
+             for m in (pa.SHARED_AUTO, pa.SHARED_PACKED)}
+    ws2 = torch.empty(max(1, max(p["workspace_bytes"] for p in plans.values())),
+                      dtype=torch.uint8, device=dev)
+
+    def shared(mode):
+        return lambda: pa.prefill_shared_prefix(
+            pool, q, cu, ctx, bt, wl.scale, wl.shared_prefix, causal=call.causal, max_q_len=mq,
+            max_ctx_len=mc, out=o, lse=lse, mode=mode, workspace=ws2)
     fns = {
         "prefill": lambda: pa.prefill(pool, q, cu, ctx, bt, wl.scale, causal=call.causal,
                                       max_q_len=mq, max_ctx_len=mc, out=o, lse=lse,
                                       num_splits=S, workspace=ws),
-        "shared_prefix": lambda: pa.prefill_shared_prefix(
-            pool, q, cu, ctx, bt, wl.scale, wl.shared_prefix, causal=call.causal, max_q_len=mq,
-            max_ctx_len=mc, out=o, lse=lse, prefix_splits=sp, suffix_splits=ss, workspace=ws2),
+        "shared_prefix": shared(pa.SHARED_AUTO),
+        "shared_prefix_packed": shared(pa.SHARED_PACKED),
     }
+    mode_name = {pa.SHARED_PACKED: "packed", pa.SHARED_PLAIN: "plain"}
     out = {"workload": wl.name, "flops": prefill_flops(call, wl.head_dim, wl.num_q_heads),
-           "splits": {"prefill": S, "shared_prefix": [sp, ss]}}
+           "splits": {"prefill": S,
+                      "shared_prefix": {mode_name[p["mode"]]: [p["prefix_splits"],
+                                                               p["suffix_splits"],
+                                                               p["plain_splits"]]
+                                        for p in plans.values()}},
+           "shared_prefix_mode": mode_name[plans[pa.SHARED_AUTO]["mode"]]}
     for name, fn in fns.items():
         for _ in range(args.warmup):
             fn()

@@ -283,54 +283,86 @@ pa_status pa_prefill_backward(const pa_kv_pool* pool, const void* q, const void*
 /* ------------------------------------------------------------ shared prefix
  * pa_prefill for a batch whose sequences all begin with the same prefix_len
  * tokens held in the same physical blocks (reference-counted sharing of a
- * common prompt's blocks: the survey page, section 3, "core principle").  The
+ * common prompt's blocks: the survey page, section 3, "core principle"; the
+ * saving it brings: same page, section 3, "performance advantages").  The
  * result is the same attention as pa_prefill with the same arguments; only
- * the work is arranged differently:
- *   1. all num_q_tokens query tokens of the batch, packed into one sequence,
- *      attend the prefix keys 0..prefix_len-1 once per KV head (no mask: every
- *      query lies past the prefix), read through block-table row 0;
- *   2. each sequence's queries attend its own keys prefix_len..ctx_len_b-1
- *      (causal as requested; when max_q_len is 1 this pass is pa_decode's
+ * the work is arranged differently.  Two arrangements (pa_shared_plan.mode):
+ *
+ * PA_SHARED_PACKED, for the rows with q_len_b = 1 (decode rows):
+ *   1. those rows of all sequences, packed into one virtual sequence (row b =
+ *      sequence b's query), attend the prefix keys 0..prefix_len-1 once per
+ *      KV head (no mask: every query lies past the prefix), read through
+ *      block-table row 0, so the prefix is multiplied in a matrix tile for all
+ *      of them together instead of streamed once per sequence;
+ *   2. each such row attends its own keys prefix_len..ctx_len_b-1 (pa_decode's
  *      split pass over the pages past the prefix);
  *   3. the normalised partials of both passes are merged by their logsumexps
  *      (the combination of partial softmax statistics of the "core modules"
  *      chapter, section 2.1).
- * So a decode row's share of the prefix is multiplied in a matrix tile with
- * the other sequences' rows instead of one sequence at a time.
+ *   Rows with q_len_b > 1 gain nothing from packing (each of their query
+ *   tiles meets every prefix key either way): they take pa_prefill's pass
+ *   over all their keys, before the packed passes.
+ * PA_SHARED_PLAIN: the whole batch as pa_decode (max_q_len = 1) or pa_prefill
+ *   would run it.
+ * PA_SHARED_AUTO (to pa_shared_prefix_plan only) packs when the prefix bytes
+ * that all but one of the q_len = 1 rows would read (bounded from the shapes:
+ * with max_q_len > 1, at most (num_seqs * max_q_len - num_q_tokens) /
+ * (max_q_len - 1) rows can have q_len = 1) reach 128 MiB, and otherwise runs
+ * plain, so that packing is taken only where it pays.
+ *
  * Arguments as pa_prefill, plus:
  *   prefix_len   : a multiple of 16, >= 16, and prefix_len + max_q_len <=
  *                  max_ctx_len (checked).
  *   num_q_tokens : cu_q_lens[num_seqs], the rows of q and o; 1 <= num_q_tokens
- *                  <= num_seqs * max_q_len (checked).  Rows of a sequence past
- *                  num_q_tokens are not written.  When max_q_len is 1 every
- *                  sequence has exactly one query (q_len_b >= 1 as for every
- *                  call), so num_q_tokens must equal num_seqs (checked).
- *   prefix_splits, suffix_splits : key splits of passes 1 and 2, 0 = choose
- *                  with pa_shared_prefix_num_splits(), at most 64 each.
- *   workspace    : at least pa_shared_prefix_workspace_bytes(num_q_tokens,
- *                  num_q_heads, head_dim, prefix_splits + suffix_splits) bytes
- *                  of device memory, 16-byte aligned (always needed).
+ *                  <= num_seqs * max_q_len (checked).  When max_q_len is 1
+ *                  every sequence has exactly one query (q_len_b >= 1 as for
+ *                  every call), so num_q_tokens must equal num_seqs (checked).
+ *   plan         : from pa_shared_prefix_plan, whose split counts the caller
+ *                  may change within their bounds (checked: packed 1..16
+ *                  prefix splits, 1..64 own-key splits, 1..16 splits of the
+ *                  q_len > 1 rows' pass; plain 1..64 for max_q_len = 1, else
+ *                  1..16), or NULL for the PA_SHARED_AUTO plan.
+ *   workspace    : at least pa_shared_prefix_workspace_bytes(pool, num_seqs,
+ *                  num_q_heads, max_q_len, plan) bytes of device memory,
+ *                  16-byte aligned (none needed when that is 0).
  * Device-resident contract (not checked): for every b, block_table[b][j] ==
  * block_table[0][j] for j < prefix_len / 16, and ctx_len_b - q_len_b >=
  * prefix_len (no query inside the prefix).  If it does not hold the result is
  * unspecified, but nothing outside the documented buffers is touched.
  * Supported: bf16 and fp8 pools (PA_ERR_UNSUPPORTED for fp32 pools).
  */
-pa_status pa_shared_prefix_num_splits(int32_t num_seqs, int32_t num_kv_heads,
-                                      int32_t num_q_heads, int32_t max_q_len,
-                                      int32_t max_ctx_len, int32_t prefix_len,
-                                      int32_t num_q_tokens, int32_t* prefix_splits,
-                                      int32_t* suffix_splits);
-size_t pa_shared_prefix_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads,
-                                        int32_t head_dim, int32_t total_splits);
+#define PA_SHARED_AUTO 0
+#define PA_SHARED_PACKED 1
+#define PA_SHARED_PLAIN 2
+
+typedef struct pa_shared_plan {
+  int32_t mode;            /* PA_SHARED_PACKED or PA_SHARED_PLAIN */
+  int32_t prefix_splits;   /* packed: key splits of the packed prefix pass */
+  int32_t suffix_splits;   /* packed: key splits of the q_len = 1 rows' own keys */
+  int32_t plain_splits;    /* key splits of pa_prefill's / pa_decode's pass */
+  size_t workspace_bytes;  /* filled by pa_shared_prefix_plan */
+} pa_shared_plan;
+
+/* Fill *plan for the given shapes: the arrangement (mode PA_SHARED_AUTO
+ * chooses as above; PACKED and PLAIN force one), its split counts and its
+ * workspace size.  PA_ERR_INVALID_ARG for shapes pa_prefill_shared_prefix
+ * would refuse, PA_ERR_UNSUPPORTED for fp32 pools. */
+pa_status pa_shared_prefix_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_q_len, int32_t max_ctx_len, int32_t prefix_len,
+                                int32_t num_q_tokens, int32_t mode, pa_shared_plan* plan);
+/* Workspace bytes for a (possibly edited) plan; 0 for an invalid plan or
+ * when none is needed. */
+size_t pa_shared_prefix_workspace_bytes(const pa_kv_pool* pool, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_q_len,
+                                        const pa_shared_plan* plan);
 pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype,
                                    void* o, float* lse, const int32_t* cu_q_lens,
                                    const int32_t* ctx_lens, const int32_t* block_table,
                                    int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_q_len, int32_t max_ctx_len, float scale,
                                    int32_t causal, int32_t prefix_len, int32_t num_q_tokens,
-                                   int32_t prefix_splits, int32_t suffix_splits,
-                                   void* workspace, size_t workspace_bytes, void* stream);
+                                   const pa_shared_plan* plan, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ decode
  * One query token per sequence, at position ctx_len_b - 1 (it sees all

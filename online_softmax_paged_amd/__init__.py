@@ -59,12 +59,22 @@ _prefill_fp8 = _sig("pa_prefill_fp8", ctypes.c_int,
                      _F, _I32, _I32, _VP, _SZ, _VP])
 _pre_splits = _sig("pa_prefill_num_splits", _I32, [_I32, _I32, _I32, _I32, _I32])
 _pre_ws = _sig("pa_prefill_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32, _I32])
-_sp_splits = _sig("pa_shared_prefix_num_splits", ctypes.c_int,
-                  [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP])
-_sp_ws = _sig("pa_shared_prefix_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
+
+
+class _SharedPlan(ctypes.Structure):
+    """pa_shared_plan."""
+    _fields_ = [("mode", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
+                ("suffix_splits", ctypes.c_int32), ("plain_splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_SPP = ctypes.POINTER(_SharedPlan)
+_sp_plan = _sig("pa_shared_prefix_plan", ctypes.c_int,
+                [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _SPP])
+_sp_ws = _sig("pa_shared_prefix_workspace_bytes", _SZ, [_P, _I32, _I32, _I32, _SPP])
 _prefill_sp = _sig("pa_prefill_shared_prefix", ctypes.c_int,
                    [_P, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
-                    _F, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP])
+                    _F, _I32, _I32, _I32, _SPP, _VP, _SZ, _VP])
 _bwd_ws = _sig("pa_backward_workspace_bytes", _SZ, [_P, _I32, _I32, _I32])
 _bwd = _sig("pa_prefill_backward", ctypes.c_int,
             [_P, _VP, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
@@ -98,7 +108,7 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_decode", "pa_allocator_create", "pa_allocator_destroy", "pa_alloc_block",
             "pa_block_incref", "pa_block_decref", "pa_block_refcount", "pa_num_free_blocks",
             "pa_append_kv", "pa_copy_blocks", "pa_plan_append", "pa_prefill_num_splits",
-            "pa_prefill_workspace_bytes", "pa_shared_prefix_num_splits",
+            "pa_prefill_workspace_bytes", "pa_shared_prefix_plan",
             "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
             "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits",
             "pa_backward_workspace_bytes", "pa_prefill_backward", "pa_prefill_fp8",
@@ -298,33 +308,41 @@ def prefill(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table, sca
     return o, lse
 
 
-def shared_prefix_num_splits(num_seqs: int, num_kv_heads: int, num_q_heads: int,
-                             max_q_len: int, max_ctx_len: int, prefix_len: int,
-                             num_q_tokens: int) -> tuple[int, int]:
-    """Key splits (prefix pass, suffix pass) that prefill_shared_prefix picks."""
-    p, s = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(_sp_splits(num_seqs, num_kv_heads, num_q_heads, max_q_len, max_ctx_len, prefix_len,
-                      num_q_tokens, ctypes.addressof(p), ctypes.addressof(s)),
-           "pa_shared_prefix_num_splits")
-    return p.value, s.value
+SHARED_AUTO, SHARED_PACKED, SHARED_PLAIN = 0, 1, 2   # PA_SHARED_*
 
 
-def shared_prefix_workspace_bytes(num_q_tokens: int, num_q_heads: int, head_dim: int,
-                                  total_splits: int) -> int:
-    return int(_sp_ws(num_q_tokens, num_q_heads, head_dim, total_splits))
+def shared_prefix_plan(pool: KVPool, num_seqs: int, num_q_heads: int, max_q_len: int,
+                       max_ctx_len: int, prefix_len: int, num_q_tokens: int,
+                       mode: int = SHARED_AUTO) -> dict:
+    """pa_shared_prefix_plan: the arrangement prefill_shared_prefix takes (SHARED_PACKED
+    or SHARED_PLAIN), its split counts and its workspace bytes."""
+    p = _SharedPlan()
+    _check(_sp_plan(pool.c, num_seqs, num_q_heads, max_q_len, max_ctx_len, prefix_len,
+                    num_q_tokens, mode, ctypes.byref(p)), "pa_shared_prefix_plan")
+    return {f: getattr(p, f) for f, _ in _SharedPlan._fields_}
+
+
+def shared_prefix_workspace_bytes(pool: KVPool, num_seqs: int, num_q_heads: int, max_q_len: int,
+                                  plan: dict) -> int:
+    p = _SharedPlan(**{k: plan[k] for k in ("mode", "prefix_splits", "suffix_splits",
+                                            "plain_splits")})
+    return int(_sp_ws(pool.c, num_seqs, num_q_heads, max_q_len, ctypes.byref(p)))
 
 
 def prefill_shared_prefix(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, block_table,
                           scale: float, prefix_len: int, causal: bool = True,
                           max_q_len: int | None = None, max_ctx_len: int | None = None,
                           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                          prefix_splits: int = 0, suffix_splits: int = 0,
+                          mode: int = SHARED_AUTO, prefix_splits: int = 0,
+                          suffix_splits: int = 0, plain_splits: int = 0,
                           workspace: torch.Tensor | None = None, validate: bool = False,
                           stream=None):
     """prefill() for sequences that all start with the same prefix_len tokens in
-    the same physical blocks: the prefix is attended once by all query tokens
-    together, each sequence's own keys separately, and the two merged.
-    Returns (o, lse) as prefill() does."""
+    the same physical blocks.  SHARED_PACKED: the q_len = 1 rows attend the
+    prefix once, packed together, and their own keys separately, the two
+    merged; rows with q_len > 1 take prefill()'s pass.  SHARED_PLAIN: the
+    whole batch as prefill() / decode().  SHARED_AUTO lets the library choose.
+    Nonzero split counts replace the plan's.  Returns (o, lse) as prefill() does."""
     B = int(ctx_lens.numel())
     T, Hq, D = q.shape
     if max_q_len is None or max_ctx_len is None or validate:
@@ -350,21 +368,23 @@ def prefill_shared_prefix(pool: KVPool, q: torch.Tensor, cu_q_lens, ctx_lens, bl
         return (out if out is not None else torch.empty_like(q),
                 lse if lse is not None else torch.empty((T, Hq), dtype=torch.float32,
                                                         device=q.device))
-    if prefix_splits == 0 or suffix_splits == 0:
-        ap, as_ = shared_prefix_num_splits(B, pool.num_kv_heads, Hq, max_q_len, max_ctx_len,
-                                           prefix_len, T)
-        prefix_splits = prefix_splits or ap
-        suffix_splits = suffix_splits or as_
-    need = shared_prefix_workspace_bytes(T, Hq, D, prefix_splits + suffix_splits)
-    if workspace is None or workspace.numel() < need:
+    plan = shared_prefix_plan(pool, B, Hq, max_q_len, max_ctx_len, prefix_len, T, mode)
+    plan["prefix_splits"] = prefix_splits or plan["prefix_splits"]
+    plan["suffix_splits"] = suffix_splits or plan["suffix_splits"]
+    plan["plain_splits"] = plain_splits or plan["plain_splits"]
+    need = shared_prefix_workspace_bytes(pool, B, Hq, max_q_len, plan)
+    if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    cplan = _SharedPlan(plan["mode"], plan["prefix_splits"], plan["suffix_splits"],
+                        plan["plain_splits"], need)
     _check(_prefill_sp(pool.c, _ptr(q), _DT[q.dtype], _ptr(o), _ptr(lse), _ptr(cu_q_lens),
                        _ptr(ctx_lens), _ptr(block_table), block_table.shape[1], B, Hq, max_q_len,
-                       max_ctx_len, scale, 1 if causal else 0, prefix_len, T, prefix_splits,
-                       suffix_splits, _ptr(workspace), workspace.numel(), _stream(stream)),
+                       max_ctx_len, scale, 1 if causal else 0, prefix_len, T,
+                       ctypes.byref(cplan), _ptr(workspace) if need else None,
+                       workspace.numel() if need else 0, _stream(stream)),
            "pa_prefill_shared_prefix")
     return o, lse
 

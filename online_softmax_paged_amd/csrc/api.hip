@@ -94,7 +94,7 @@ const char* pa_status_string(pa_status s) {
   return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return 7; }
+int32_t pa_abi_version(void) { return 8; }
 
 size_t pa_write_kv_workspace_bytes(const pa_kv_pool* pool) {
   if (!pool || pool->kv_dtype != PA_FP8_E4M3 || pool->num_blocks < 1) return 0;
@@ -261,32 +261,129 @@ pa_status pa_prefill_fp8(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype
                       workspace, workspace_bytes, stream, true);
 }
 
-pa_status pa_shared_prefix_num_splits(int32_t num_seqs, int32_t num_kv_heads,
-                                      int32_t num_q_heads, int32_t max_q_len,
-                                      int32_t max_ctx_len, int32_t prefix_len,
-                                      int32_t num_q_tokens, int32_t* prefix_splits,
-                                      int32_t* suffix_splits) {
-  if (!prefix_splits || !suffix_splits || num_seqs < 1 || num_q_tokens < 1 ||
-      prefix_len < 1 || max_ctx_len <= prefix_len)
+// Rows with q_len = 1 that a batch can hold at most: every other sequence
+// has 2 .. max_q_len queries.
+static int64_t most_single_rows(int32_t num_seqs, int32_t max_q_len, int32_t num_q_tokens) {
+  if (max_q_len == 1) return num_seqs;
+  int64_t n = (static_cast<int64_t>(num_seqs) * max_q_len - num_q_tokens) / (max_q_len - 1);
+  return n < 0 ? 0 : (n > num_seqs ? num_seqs : n);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace of a shared-prefix plan, in order: gathered q_len = 1 rows (mixed
+// batches), partial outputs and logsumexps of the packed passes, partials of
+// the rows with q_len > 1 (mixed batches, plain_splits > 1).  Plain mode uses
+// pa_decode's or pa_prefill's workspace.
+struct SpLayout {
+  size_t qd, o, lse, rest, total;
+};
+static SpLayout shared_layout(const pa_shared_plan& p, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t head_dim, int32_t max_q_len) {
+  SpLayout L{};
+  if (p.mode == PA_SHARED_PLAIN) {
+    L.total = max_q_len == 1
+                  ? pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, p.plain_splits)
+                  : pa_prefill_workspace_bytes(num_seqs, max_q_len, num_q_heads, head_dim,
+                                               p.plain_splits);
+    return L;
+  }
+  const bool mixed = max_q_len > 1;
+  const size_t rows = static_cast<size_t>(p.prefix_splits + p.suffix_splits) * num_seqs *
+                      num_q_heads;
+  size_t off = 0;
+  L.qd = off;
+  off += mixed ? align256(static_cast<size_t>(num_seqs) * num_q_heads * head_dim * 2) : 0;
+  L.o = off;
+  off += align256(rows * head_dim * sizeof(float));
+  L.lse = off;
+  off += align256(rows * sizeof(float));
+  L.rest = off;
+  if (mixed)
+    off += pa_prefill_workspace_bytes(num_seqs, max_q_len, num_q_heads, head_dim, p.plain_splits);
+  L.total = off;
+  return L;
+}
+
+static pa_status check_shared_shape(const pa_kv_pool* pool, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t max_q_len, int32_t max_ctx_len,
+                                    int32_t prefix_len, int32_t num_q_tokens) {
+  pa_status s = check_pool(pool);
+  if (s != PA_OK) return s;
+  if (pool->kv_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || num_q_heads < pool->num_kv_heads || num_q_heads % pool->num_kv_heads != 0)
     return PA_ERR_INVALID_ARG;
-  // The packed pass is one sequence of all query tokens over the prefix; the
-  // suffix pass is the batch over what follows it (the decode kernel's pass
-  // when every sequence has one query).
-  *prefix_splits = pa_prefill_num_splits(1, num_kv_heads, num_q_heads, num_q_tokens, prefix_len);
-  *suffix_splits =
-      max_q_len == 1
-          ? pa_decode_num_splits(num_seqs, num_kv_heads, max_ctx_len - prefix_len)
-          : pa_prefill_num_splits(num_seqs, num_kv_heads, num_q_heads, max_q_len,
-                                  max_ctx_len - prefix_len);
+  if (max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
+  if (prefix_len < PA_BLOCK_SIZE || prefix_len % PA_BLOCK_SIZE != 0 ||
+      prefix_len + max_q_len > max_ctx_len)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_tokens < 1 ||
+      static_cast<int64_t>(num_q_tokens) > static_cast<int64_t>(num_seqs) * max_q_len)
+    return PA_ERR_INVALID_ARG;
+  // With one query per sequence, row b is sequence b's query.
+  if (max_q_len == 1 && num_q_tokens != num_seqs) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
-size_t pa_shared_prefix_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads,
-                                        int32_t head_dim, int32_t total_splits) {
-  if (num_q_tokens < 1 || num_q_heads < 1 || head_dim < 1 || total_splits < 1) return 0;
-  const size_t rows = static_cast<size_t>(total_splits) * num_q_tokens * num_q_heads;
-  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
-  return o_bytes + rows * sizeof(float);
+pa_status pa_shared_prefix_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_q_len, int32_t max_ctx_len, int32_t prefix_len,
+                                int32_t num_q_tokens, int32_t mode, pa_shared_plan* plan) {
+  if (!plan) return PA_ERR_INVALID_ARG;
+  pa_status s = check_shared_shape(pool, num_seqs, num_q_heads, max_q_len, max_ctx_len,
+                                   prefix_len, num_q_tokens);
+  if (s != PA_OK) return s;
+  if (mode != PA_SHARED_AUTO && mode != PA_SHARED_PACKED && mode != PA_SHARED_PLAIN)
+    return PA_ERR_INVALID_ARG;
+  const int32_t Hkv = pool->num_kv_heads;
+  if (mode == PA_SHARED_AUTO) {
+    // Packing saves the prefix reads of all but one of the q_len = 1 rows and
+    // costs three more launches (prefix pass, merge, and for a mixed batch
+    // the gather) plus partial traffic, about 10-15 us.  Rows with q_len > 1
+    // gain nothing: their tiles meet every prefix key either way.  So pack
+    // only when the prefix bytes the q_len = 1 rows would read beyond the
+    // first are well above that cost (128 MiB, about 20 us at 6.5 TB/s).
+    // 64 rows x 4096-token bf16 prefix (1 GiB saved): 55.2 us packed against
+    // 128.9 us; 16 rows x 1024 fp8 (31 MB): 36.3 against 26.2 us.
+    const int64_t n1 = most_single_rows(num_seqs, max_q_len, num_q_tokens);
+    const double es = pool->kv_dtype == PA_FP8_E4M3 ? 1.0 : 2.0;
+    const double saved = static_cast<double>(n1 - 1) * prefix_len * Hkv * pool->head_dim * 2.0 * es;
+    mode = (n1 >= 2 && saved >= 128.0 * (1 << 20)) ? PA_SHARED_PACKED : PA_SHARED_PLAIN;
+  }
+  plan->mode = mode;
+  if (mode == PA_SHARED_PLAIN) {
+    plan->prefix_splits = plan->suffix_splits = 0;
+    plan->plain_splits =
+        max_q_len == 1
+            ? pa_decode_num_splits(num_seqs, Hkv, max_ctx_len)
+            : pa_prefill_num_splits(num_seqs, Hkv, num_q_heads, max_q_len, max_ctx_len);
+  } else {
+    plan->prefix_splits = pa_prefill_num_splits(1, Hkv, num_q_heads, num_seqs, prefix_len);
+    plan->suffix_splits = pa_decode_num_splits(num_seqs, Hkv, max_ctx_len - prefix_len);
+    plan->plain_splits =
+        max_q_len == 1
+            ? 1
+            : pa_prefill_num_splits(num_seqs, Hkv, num_q_heads, max_q_len, max_ctx_len);
+  }
+  plan->workspace_bytes =
+      shared_layout(*plan, num_seqs, num_q_heads, pool->head_dim, max_q_len).total;
+  return PA_OK;
+}
+
+static bool plan_ok(const pa_shared_plan& p, int32_t max_q_len) {
+  if (p.mode == PA_SHARED_PLAIN)
+    return p.plain_splits >= 1 && p.plain_splits <= (max_q_len == 1 ? 64 : 16);
+  if (p.mode != PA_SHARED_PACKED) return false;
+  return p.prefix_splits >= 1 && p.prefix_splits <= 16 && p.suffix_splits >= 1 &&
+         p.suffix_splits <= 64 && p.plain_splits >= 1 && p.plain_splits <= 16;
+}
+
+size_t pa_shared_prefix_workspace_bytes(const pa_kv_pool* pool, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_q_len,
+                                        const pa_shared_plan* plan) {
+  if (!plan || check_pool(pool) != PA_OK || num_seqs < 1 || num_q_heads < 1 || max_q_len < 1 ||
+      !plan_ok(*plan, max_q_len))
+    return 0;
+  return shared_layout(*plan, num_seqs, num_q_heads, pool->head_dim, max_q_len).total;
 }
 
 pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dtype q_dtype,
@@ -295,48 +392,57 @@ pa_status pa_prefill_shared_prefix(const pa_kv_pool* pool, const void* q, pa_dty
                                    int32_t bt_stride, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_q_len, int32_t max_ctx_len, float scale,
                                    int32_t causal, int32_t prefix_len, int32_t num_q_tokens,
-                                   int32_t prefix_splits, int32_t suffix_splits,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   const pa_shared_plan* plan, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   if (num_seqs == 0 && pool) return check_pool(pool);
   pa_status s = check_attn(pool, q, q_dtype, o, ctx_lens, block_table, bt_stride, num_seqs,
                            num_q_heads, max_ctx_len, scale);
   if (s != PA_OK) return s;
-  if (pool->kv_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
-  if (!cu_q_lens || max_q_len < 1 || max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
-  if (prefix_len < PA_BLOCK_SIZE || prefix_len % PA_BLOCK_SIZE != 0 ||
-      prefix_len + max_q_len > max_ctx_len)
-    return PA_ERR_INVALID_ARG;
-  if (num_q_tokens < 1 || static_cast<int64_t>(num_q_tokens) >
-                              static_cast<int64_t>(num_seqs) * max_q_len)
-    return PA_ERR_INVALID_ARG;
-  if (prefix_splits < 0 || prefix_splits > 64 || suffix_splits < 0 || suffix_splits > 64)
-    return PA_ERR_INVALID_ARG;
-  // With one query per sequence the suffix pass is the decode kernel, which
-  // takes query row b as sequence b's query: the rows must be one per sequence.
-  if (max_q_len == 1 && num_q_tokens != num_seqs) return PA_ERR_INVALID_ARG;
-  int32_t auto_p = 1, auto_s = 1;
-  s = pa_shared_prefix_num_splits(num_seqs, pool->num_kv_heads, num_q_heads, max_q_len,
-                                  max_ctx_len, prefix_len, num_q_tokens, &auto_p, &auto_s);
+  if (!cu_q_lens) return PA_ERR_INVALID_ARG;
+  s = check_shared_shape(pool, num_seqs, num_q_heads, max_q_len, max_ctx_len, prefix_len,
+                         num_q_tokens);
   if (s != PA_OK) return s;
-  if (prefix_splits == 0) prefix_splits = auto_p;
-  if (suffix_splits == 0) suffix_splits = auto_s;
-  const int32_t total = prefix_splits + suffix_splits;
-  const size_t need =
-      pa_shared_prefix_workspace_bytes(num_q_tokens, num_q_heads, pool->head_dim, total);
-  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  pa_shared_plan p;
+  if (plan) {
+    p = *plan;
+    if (!plan_ok(p, max_q_len)) return PA_ERR_INVALID_ARG;
+  } else {
+    s = pa_shared_prefix_plan(pool, num_seqs, num_q_heads, max_q_len, max_ctx_len, prefix_len,
+                              num_q_tokens, PA_SHARED_AUTO, &p);
+    if (s != PA_OK) return s;
+  }
+  if (p.mode == PA_SHARED_PLAIN) {
+    if (max_q_len == 1)
+      return pa_decode(pool, q, q_dtype, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
+                       num_q_heads, max_ctx_len, scale, p.plain_splits, workspace,
+                       workspace_bytes, stream);
+    return prefill_impl(pool, q, q_dtype, o, lse, cu_q_lens, ctx_lens, block_table, bt_stride,
+                        num_seqs, num_q_heads, max_q_len, max_ctx_len, scale, causal,
+                        p.plain_splits, workspace, workspace_bytes, stream, false);
+  }
+  const SpLayout L = shared_layout(p, num_seqs, num_q_heads, pool->head_dim, max_q_len);
+  if (!workspace || workspace_bytes < L.total) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
   AttnArgs a = make_args(pool, q, o, lse, ctx_lens, block_table, bt_stride, num_seqs,
                          num_q_heads, max_ctx_len, scale);
   a.cu_q_lens = cu_q_lens;
   a.max_q_len = max_q_len;
   a.causal = causal ? 1 : 0;
-  const size_t rows = static_cast<size_t>(total) * num_q_tokens * num_q_heads;
-  const size_t o_bytes = (rows * pool->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-  a.part_rows = num_q_tokens;
-  return launched(launch_prefill_shared_prefix(a, prefix_len, num_q_tokens, prefix_splits,
-                                               suffix_splits, static_cast<hipStream_t>(stream)));
+  char* w = static_cast<char*>(workspace);
+  SharedLaunch sl{};
+  sl.prefix_len = prefix_len;
+  sl.s_prefix = p.prefix_splits;
+  sl.s_suffix = p.suffix_splits;
+  sl.s_plain = max_q_len > 1 ? p.plain_splits : 1;
+  sl.qd = max_q_len > 1 ? w + L.qd : nullptr;
+  sl.ws_o = reinterpret_cast<float*>(w + L.o);
+  sl.ws_lse = reinterpret_cast<float*>(w + L.lse);
+  if (max_q_len > 1 && sl.s_plain > 1) {
+    const size_t rows = static_cast<size_t>(sl.s_plain) * num_seqs * max_q_len * num_q_heads;
+    sl.ws_o2 = reinterpret_cast<float*>(w + L.rest);
+    sl.ws_lse2 = reinterpret_cast<float*>(w + L.rest + align256(rows * pool->head_dim * 4));
+  }
+  return launched(launch_prefill_shared_prefix(a, sl, static_cast<hipStream_t>(stream)));
 }
 
 size_t pa_backward_workspace_bytes(const pa_kv_pool* pool, int32_t num_seqs,

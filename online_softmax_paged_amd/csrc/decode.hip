@@ -201,6 +201,8 @@ void decode_split_kernel(AttnArgs a) {
   const int c = lane & 15, grp = lane >> 4;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
   const int S = a.num_splits;
+  // the q_len = 1 rows of a mixed batch: q row b is sequence b's query
+  if (a.q_filter == kQOne && a.cu_q_lens[b + 1] - a.cu_q_lens[b] != 1) return;
 
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);

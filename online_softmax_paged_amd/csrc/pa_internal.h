@@ -145,7 +145,15 @@ struct AttnArgs {
   // Prefill of an fp8 pool with Q and P quantised to E4M3 and both products
   // on the fp8 MFMA (no packed_q or key_begin).
   int32_t fp8_mma;
+  // Row filter by query count q_len_b = cu_q_lens[b+1] - cu_q_lens[b]
+  // (kQAll: every sequence).  kQOne: only sequences with q_len_b = 1 (the
+  // decode split pass and the merge); kQMany: only sequences with
+  // q_len_b > 1 (the prefill pass and the merge).  The others are skipped:
+  // nothing is read or written for them.
+  int32_t q_filter;
 };
+
+constexpr int32_t kQAll = 0, kQOne = 1, kQMany = 2;
 
 // One buffer load of 16 bytes per lane straight into LDS: lane i's bytes
 // [voffset, voffset + 16) of the buffer [base, base + nbytes) land at
@@ -353,8 +361,20 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t st);
 // The decode split pass alone (bf16 or fp8 pool), partials as a's workspace says.
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t st);
-hipError_t launch_prefill_shared_prefix(const AttnArgs& a, int prefix_len, int num_q_tokens,
-                                        int s_prefix, int s_suffix, hipStream_t st);
+// The packed passes of a shared-prefix call: the rows with q_len = 1 attend
+// the prefix packed together (one row per sequence) and their own keys
+// through the decode split pass, and the two are merged; in a batch that
+// also holds rows with q_len > 1, those take the ordinary prefill pass first.
+struct SharedLaunch {
+  int prefix_len;
+  int s_prefix, s_suffix, s_plain;  // key splits of the three passes
+  void* qd;                         // q_len = 1 rows gathered ([B][Hq][D] bf16), mixed batches
+  float* ws_o;                      // partials of the prefix and own-key passes,
+  float* ws_lse;                    //   (s_prefix + s_suffix) x B x Hq rows
+  float* ws_o2;                     // partials of the q_len > 1 rows when s_plain > 1
+  float* ws_lse2;
+};
+hipError_t launch_prefill_shared_prefix(const AttnArgs& a, const SharedLaunch& L, hipStream_t st);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t st);
 
 }  // namespace pa

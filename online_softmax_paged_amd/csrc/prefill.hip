@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
   }
   const int t0 = tile * TQ;
-  if (t0 >= qlen) return;
+  if (t0 >= qlen || (a.q_filter == kQMany && qlen == 1)) return;
   const int pos_base = ctx - qlen;            // position of query token 0
   const int t_last = min(t0 + TQ, qlen) - 1;  // last token of this tile
   // Inconsistent lengths (ctx = 0, or q_len > ctx) leave some or all rows
@@ -582,7 +582,7 @@ void prefill_dma_kernel(AttnArgs a, int n_tiles) {
     ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
   }
   const int t0 = tile * TQ;
-  if (t0 >= qlen) return;
+  if (t0 >= qlen || (a.q_filter == kQMany && qlen == 1)) return;
   const int pos_base = ctx - qlen;
   const int t_last = min(t0 + TQ, qlen) - 1;
   const int kmax = max(0, a.causal ? min(ctx, pos_base + t_last + 1) : ctx);  // 0: rows left empty
@@ -940,7 +940,7 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx_len ? a.max_ctx_len : ctx);
   const int t0 = tile * TQ;
-  if (t0 >= qlen) return;
+  if (t0 >= qlen || (a.q_filter == kQMany && qlen == 1)) return;
   const int pos_base = ctx - qlen;
   const int t_last = min(t0 + TQ, qlen) - 1;
   const int kmax = max(0, a.causal ? min(ctx, pos_base + t_last + 1) : ctx);  // 0: rows left empty
@@ -1288,15 +1288,20 @@ template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int Hq = a.num_q_heads, S = a.num_splits;
-  const int64_t per_seq = static_cast<int64_t>(a.max_q_len) * Hq;
+  // kQOne: one row per sequence, partial row b (the packed rows of the
+  // q_len = 1 sequences), written to the sequence's token.
+  const int64_t per_seq = static_cast<int64_t>(a.q_filter == kQOne ? 1 : a.max_q_len) * Hq;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (r >= per_seq * a.num_seqs) return;
   const int b = static_cast<int>(r / per_seq);
   const int i = static_cast<int>((r % per_seq) / Hq), h = static_cast<int>(r % Hq);
-  const int q0 = a.cu_q_lens[b];
-  if (i >= a.cu_q_lens[b + 1] - q0) return;
-  const int64_t row = static_cast<int64_t>(q0 + i) * Hq + h;  // token row, as in the partials
-  const int64_t stride = a.part_rows * Hq;                     // partial rows per split
+  const int q0 = a.cu_q_lens[b], qlen = a.cu_q_lens[b + 1] - q0;
+  if (i >= qlen) return;
+  if ((a.q_filter == kQOne && qlen != 1) || (a.q_filter == kQMany && qlen == 1)) return;
+  const int64_t out_row = static_cast<int64_t>(q0 + i) * Hq + h;  // token row of o and lse
+  // the row of the partials: the token's, or the sequence's under kQOne
+  const int64_t row = a.q_filter == kQOne ? static_cast<int64_t>(b) * Hq + h : out_row;
+  const int64_t stride = a.part_rows * Hq;  // partial rows per split
   if (row >= stride) return;
   // lane s holds split s's logsumexp and weight (64 splits at a time)
   float M = -INFINITY;
@@ -1341,8 +1346,26 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
   const float inv = empty ? 0.f : 1.f / W;
 #pragma unroll
   for (int j = 0; j < NPL; ++j)
-    static_cast<uint16_t*>(a.o)[row * D + lane + 64 * j] = to_bf16_bits(acc[j] * inv);
-  if (lane == 0 && a.lse) a.lse[row] = empty ? -INFINITY : M + __logf(W);
+    static_cast<uint16_t*>(a.o)[out_row * D + lane + 64 * j] = to_bf16_bits(acc[j] * inv);
+  if (lane == 0 && a.lse) a.lse[out_row] = empty ? -INFINITY : M + __logf(W);
+}
+
+// The query rows of the sequences with q_len_b = 1, one per sequence:
+// qd[b] = q[cu_q_lens[b]] for those sequences, zeros for the others (all
+// heads, bf16).  One workgroup per sequence, 16 bytes per lane.
+__global__ __launch_bounds__(256) void gather_q1_rows_kernel(const u32x4* __restrict__ q,
+                                                             const int32_t* __restrict__ cu,
+                                                             int row16, u32x4* __restrict__ qd) {
+  const int b = blockIdx.x;
+  const int q0 = cu[b];
+  const bool one = cu[b + 1] - q0 == 1;
+  u32x4* dst = qd + static_cast<int64_t>(b) * row16;
+  if (one) {
+    const u32x4* src = q + static_cast<int64_t>(q0) * row16;
+    for (int i = threadIdx.x; i < row16; i += 256) dst[i] = src[i];
+  } else {
+    for (int i = threadIdx.x; i < row16; i += 256) dst[i] = u32x4{0, 0, 0, 0};
+  }
 }
 
 // One pass of the bf16 or fp8 kernel over a's sequences (or its packed
@@ -1373,7 +1396,8 @@ hipError_t launch_pass(const AttnArgs& a, hipStream_t st) {
 // Merge of the S = a.num_splits partials of every query row into o and lse.
 template <int D>
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
-  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.max_q_len * a.num_q_heads;
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * (a.q_filter == kQOne ? 1 : a.max_q_len) *
+                       a.num_q_heads;
   prefill_merge_kernel<D><<<static_cast<unsigned>((rows + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
 }
@@ -1390,34 +1414,73 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
   return launch_merge<D>(a, st);
 }
 
-// Shared prefix: the first prefix_len keys (whole pages, the same physical
-// blocks for every sequence) are attended once by all query tokens packed
-// into one virtual sequence (no mask: every query lies past the prefix),
-// into partials 0..s_prefix-1; each sequence's own keys from prefix_len on
-// go to partials s_prefix..s_prefix+s_suffix-1; the merge combines them.
+// Shared prefix, packed: the first prefix_len keys (whole pages, the same
+// physical blocks for every sequence) are attended once by the q_len = 1 rows
+// of all sequences packed into one virtual sequence of B rows (row b is
+// sequence b's query; zeros for the other sequences, whose partials are never
+// read), with no mask since every query lies past the prefix, into partials
+// 0..s_prefix-1; each of those rows' own keys from prefix_len on go through
+// the decode split pass into partials s_prefix..s_prefix+s_suffix-1; the
+// merge combines them into the rows' tokens.  Rows with q_len > 1 take the
+// ordinary pass over all their keys (their work is the same packed or not).
 template <int D>
-hipError_t launch_shared_prefix_d(const AttnArgs& a, int prefix_len, int num_q_tokens,
-                                  int s_prefix, int s_suffix, hipStream_t st) {
+hipError_t launch_shared_prefix_d(const AttnArgs& a, const SharedLaunch& L, hipStream_t st) {
+  const bool mixed = a.max_q_len > 1;
+  hipError_t e;
+  const void* q1 = a.q;
+  if (mixed) {
+    AttnArgs c = a;
+    c.q_filter = kQMany;
+    c.num_splits = L.s_plain;
+    c.split_base = 0;
+    c.ws_o = L.s_plain > 1 ? L.ws_o2 : nullptr;
+    c.ws_lse = L.s_plain > 1 ? L.ws_lse2 : nullptr;
+    c.part_rows = static_cast<int64_t>(a.num_seqs) * a.max_q_len;
+    e = launch_pass<D>(c, st);
+    if (e != hipSuccess) return e;
+    if (L.s_plain > 1) {
+      e = launch_merge<D>(c, st);
+      if (e != hipSuccess) return e;
+    }
+    gather_q1_rows_kernel<<<a.num_seqs, 256, 0, st>>>(
+        static_cast<const u32x4*>(a.q), a.cu_q_lens, a.num_q_heads * D / 8,
+        static_cast<u32x4*>(L.qd));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    q1 = L.qd;
+  }
   AttnArgs p = a;
-  p.packed_q = num_q_tokens;
-  p.max_ctx_len = prefix_len;
+  p.q = q1;
+  p.ws_o = L.ws_o;
+  p.ws_lse = L.ws_lse;
+  p.part_rows = a.num_seqs;
+  p.q_filter = kQAll;
+  p.packed_q = a.num_seqs;
+  p.max_ctx_len = L.prefix_len;
   p.causal = 0;
   p.key_begin = 0;
   p.split_base = 0;
-  p.num_splits = s_prefix;
-  hipError_t e = launch_pass<D>(p, st);
+  p.num_splits = L.s_prefix;
+  e = launch_pass<D>(p, st);
   if (e != hipSuccess) return e;
-  AttnArgs q = a;
-  q.packed_q = 0;
-  q.key_begin = prefix_len;
-  q.split_base = s_prefix;
-  q.num_splits = s_suffix;
-  // one query per sequence: the suffixes go through the decode kernel, which
-  // streams pages for a single row instead of multiplying a 128-row tile
-  e = a.max_q_len == 1 ? launch_decode_split(q, st) : launch_pass<D>(q, st);
+  AttnArgs s = a;
+  s.q = q1;
+  s.ws_o = L.ws_o;
+  s.ws_lse = L.ws_lse;
+  s.part_rows = a.num_seqs;
+  s.q_filter = mixed ? kQOne : kQAll;
+  s.packed_q = 0;
+  s.key_begin = L.prefix_len;
+  s.split_base = L.s_prefix;
+  s.num_splits = L.s_suffix;
+  e = launch_decode_split(s, st);
   if (e != hipSuccess) return e;
   AttnArgs m = a;
-  m.num_splits = s_prefix + s_suffix;
+  m.ws_o = L.ws_o;
+  m.ws_lse = L.ws_lse;
+  m.part_rows = a.num_seqs;
+  m.q_filter = kQOne;
+  m.num_splits = L.s_prefix + L.s_suffix;
   return launch_merge<D>(m, st);
 }
 
@@ -1427,11 +1490,9 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t st) {
   return a.head_dim == 64 ? launch_prefill_d<64>(a, st) : launch_prefill_d<128>(a, st);
 }
 
-hipError_t launch_prefill_shared_prefix(const AttnArgs& a, int prefix_len, int num_q_tokens,
-                                        int s_prefix, int s_suffix, hipStream_t st) {
-  return a.head_dim == 64
-             ? launch_shared_prefix_d<64>(a, prefix_len, num_q_tokens, s_prefix, s_suffix, st)
-             : launch_shared_prefix_d<128>(a, prefix_len, num_q_tokens, s_prefix, s_suffix, st);
+hipError_t launch_prefill_shared_prefix(const AttnArgs& a, const SharedLaunch& L, hipStream_t st) {
+  return a.head_dim == 64 ? launch_shared_prefix_d<64>(a, L, st)
+                          : launch_shared_prefix_d<128>(a, L, st);
 }
 
 }  // namespace pa

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert pa.abi_version() == 7
+    assert pa.abi_version() == 8
     assert pa.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert pa.status_string(s) and pa.status_string(s) != "unknown status"
@@ -171,41 +171,87 @@ def test_prefill_split_checks_and_heuristic():
     assert pa.prefill_num_splits(1, 1, 1, 10, 100) == 1
 
 
-def _shared(pool, **kw):
+def _shared(pool, plan=(1, 1, 1, 1), **kw):
+    """pa_prefill_shared_prefix through the C ABI; plan = (mode, prefix, suffix,
+    plain splits) or None for the library's choice."""
     a = dict(q=0x5000, q_dtype=pa.PA_BF16, o=0x6000, lse=0x7000, cu=0x8000, ctx=0x9000,
              bt=0xa000, stride=8, B=2, Hq=8, max_q=32, max_ctx=128, scale=0.1, causal=1,
-             prefix=64, T=40, sp=1, ss=1, ws=0, ws_bytes=0)
+             prefix=64, T=40, ws=0, ws_bytes=0)
     a.update(kw)
+    cp = None if plan is None else ctypes.byref(pa._SharedPlan(*plan, 0))
     return pa._prefill_sp(pool.c, a["q"], a["q_dtype"], a["o"], a["lse"], a["cu"], a["ctx"],
                           a["bt"], a["stride"], a["B"], a["Hq"], a["max_q"], a["max_ctx"],
-                          a["scale"], a["causal"], a["prefix"], a["T"], a["sp"], a["ss"],
-                          a["ws"], a["ws_bytes"], None)
+                          a["scale"], a["causal"], a["prefix"], a["T"], cp, a["ws"],
+                          a["ws_bytes"], None)
+
+
+def _plan(**kw):
+    return dict(zip(("mode", "prefix_splits", "suffix_splits", "plain_splits"),
+                    kw.get("t", (pa.SHARED_PACKED, 1, 1, 1))))
 
 
 def test_shared_prefix_checks():
-    need = pa.shared_prefix_workspace_bytes(40, 8, 128, 2)
-    assert need >= 2 * 40 * 8 * (128 + 1) * 4
-    assert pa.shared_prefix_workspace_bytes(0, 8, 128, 2) == 0
     p = _FakePool()
+    # packed, mixed batch: gathered decode rows + partials of both packed passes
+    need = pa.shared_prefix_workspace_bytes(p, 2, 8, 32, _plan())
+    assert need >= 2 * 8 * 128 * 2 + 2 * 2 * 8 * (128 + 1) * 4
+    need3 = pa.shared_prefix_workspace_bytes(p, 2, 8, 32, _plan(t=(pa.SHARED_PACKED, 1, 1, 3)))
+    assert need3 >= need + 3 * 2 * 32 * 8 * (128 + 1) * 4   # partials of the q_len > 1 rows
+    # packed, decode rows only: no gather
+    assert pa.shared_prefix_workspace_bytes(p, 2, 8, 1, _plan()) >= 2 * 2 * 8 * 129 * 4
+    # plain: pa_decode's / pa_prefill's workspace
+    assert pa.shared_prefix_workspace_bytes(p, 2, 8, 1, _plan(t=(pa.SHARED_PLAIN, 0, 0, 1))) == 0
+    assert (pa.shared_prefix_workspace_bytes(p, 2, 8, 32, _plan(t=(pa.SHARED_PLAIN, 0, 0, 3)))
+            == pa.prefill_workspace_bytes(2, 32, 8, 128, 3))
+    for bad in ((3, 1, 1, 1), (pa.SHARED_AUTO, 1, 1, 1), (pa.SHARED_PACKED, 17, 1, 1),
+                (pa.SHARED_PACKED, 1, 65, 1), (pa.SHARED_PACKED, 1, 0, 1),
+                (pa.SHARED_PACKED, 1, 1, 17), (pa.SHARED_PLAIN, 0, 0, 17)):
+        assert pa.shared_prefix_workspace_bytes(p, 2, 8, 32, _plan(t=bad)) == 0, bad
+        assert _shared(p, plan=bad, ws=0x10000, ws_bytes=1 << 30) == pa.PA_ERR_INVALID_ARG, bad
     assert _shared(_FakePool(kv_dtype=pa.PA_F32), q_dtype=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
-    assert _shared(p) == pa.PA_ERR_WORKSPACE                       # always needs a workspace
+    assert _shared(p) == pa.PA_ERR_WORKSPACE                       # packed needs a workspace
     assert _shared(p, ws=0x10000, ws_bytes=need - 1) == pa.PA_ERR_WORKSPACE
     assert _shared(p, ws=0x10008, ws_bytes=need) == pa.PA_ERR_INVALID_ARG   # misaligned
+    assert _shared(p, plan=(pa.SHARED_PLAIN, 0, 0, 3)) == pa.PA_ERR_WORKSPACE
     for bad in (dict(prefix=0), dict(prefix=24), dict(prefix=112),  # not whole pages; no room
-                dict(T=0), dict(T=65), dict(sp=65), dict(ss=-1), dict(cu=0),
-                dict(max_q=0)):
+                dict(T=0), dict(T=65), dict(cu=0), dict(max_q=0)):
         assert _shared(p, **bad) == pa.PA_ERR_INVALID_ARG, bad
+        assert _shared(p, plan=None, **bad) == pa.PA_ERR_INVALID_ARG, bad
     assert _shared(p, B=0) == pa.PA_OK
-    # one query per sequence: the decode suffix pass takes row b as sequence b
+    # one query per sequence: the decode pass takes row b as sequence b
     assert _shared(p, max_q=1, T=1) == pa.PA_ERR_INVALID_ARG
     assert _shared(p, max_q=1, T=2) == pa.PA_ERR_WORKSPACE        # rows == sequences: accepted
-    # split choice: the packed prefix pass has few query tiles, so its keys split
-    sp, ss = pa.shared_prefix_num_splits(8, 8, 32, 1, 32768, 32768 - 64, 8)
-    assert sp > 1 and ss == 1
-    sp, ss = pa.shared_prefix_num_splits(16, 8, 32, 256, 1536, 1024, 2056)
-    assert sp == 1 and ss == 1
     with pytest.raises(pa.PAError):
-        pa.shared_prefix_num_splits(1, 8, 32, 1, 64, 64, 1)
+        pa.shared_prefix_plan(p, 1, 8, 1, 64, 64, 1)             # no room past the prefix
+    with pytest.raises(pa.PAError):
+        pa.shared_prefix_plan(p, 2, 8, 32, 128, 64, 40, mode=7)
+
+
+def test_shared_prefix_plan_choice():
+    """Packing is chosen only where the prefix reads it saves outweigh its
+    extra passes; a forced mode is kept."""
+    bf16 = _FakePool(num_kv_heads=8, num_blocks=1 << 16)
+    fp8 = _FakePool(num_kv_heads=8, num_blocks=1 << 16, kv_dtype=pa.PA_FP8_E4M3)
+    # 64 decode rows over a 4096-token bf16 prefix: 1 GiB of prefix reads saved
+    pl = pa.shared_prefix_plan(bf16, 64, 32, 1, 4608, 4096, 64)
+    assert pl["mode"] == pa.SHARED_PACKED and pl["workspace_bytes"] > 0
+    # 16 decode rows over a 1024-token fp8 prefix: 31 MB, not worth the passes
+    assert pa.shared_prefix_plan(fp8, 16, 32, 1, 1536, 1024, 16)["mode"] == pa.SHARED_PLAIN
+    # the mixed fp8 step (8 chunks of 256 and 8 decode rows): at most 8 rows
+    # can be decode rows, so plain
+    pl = pa.shared_prefix_plan(fp8, 16, 32, 256, 1536, 1024, 2056)
+    assert pl["mode"] == pa.SHARED_PLAIN and pl["plain_splits"] == 1
+    # 64 decode rows and one 256-token chunk over a 4096-token prefix: packed
+    pl = pa.shared_prefix_plan(bf16, 65, 32, 256, 4608, 4096, 320)
+    assert pl["mode"] == pa.SHARED_PACKED
+    # forced modes are kept
+    assert pa.shared_prefix_plan(fp8, 16, 32, 256, 1536, 1024, 2056,
+                                 mode=pa.SHARED_PACKED)["mode"] == pa.SHARED_PACKED
+    assert pa.shared_prefix_plan(bf16, 64, 32, 1, 4608, 4096, 64,
+                                 mode=pa.SHARED_PLAIN)["mode"] == pa.SHARED_PLAIN
+    # the packed prefix pass has few query tiles, so its keys split
+    pl = pa.shared_prefix_plan(bf16, 8, 32, 1, 32768, 32768 - 64, 8, mode=pa.SHARED_PACKED)
+    assert pl["prefix_splits"] > 1 and pl["suffix_splits"] == 1
 
 
 def _backward(pool, **kw):

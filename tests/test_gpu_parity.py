@@ -422,24 +422,33 @@ SHARED_CASES = [
     ("fp8", 128, 8, 2, 64, (200, 130, 300, 65), (64, 1, 100, 1), True),
     ("fp8", 128, 8, 1, 48, (90, 333, 61), (17, 200, 1), True),
     ("fp8", 64, 4, 4, 128, (129, 140, 700, 300), (1, 12, 1, 172), False),
+    ("bf16", 128, 8, 2, 64, (200, 130, 300, 65), (1, 1, 1, 1), True),       # decode rows only
+    ("fp8", 128, 16, 2, 32, (90, 33, 61, 140, 47), (1, 1, 1, 1, 1), True),
 ]
+
+# (mode, prefix, suffix, plain splits); 0 = the plan's
+SHARED_PLANS = [(pa.SHARED_PACKED, 0, 0, 0), (pa.SHARED_PACKED, 1, 1, 1),
+                (pa.SHARED_PACKED, 3, 2, 2), (pa.SHARED_PLAIN, 0, 0, 0),
+                (pa.SHARED_PLAIN, 0, 0, 3), (pa.SHARED_AUTO, 0, 0, 0)]
 
 
 @pytest.mark.parametrize("kv,D,Hq,Hkv,prefix,ctx,ql,causal", SHARED_CASES)
-@pytest.mark.parametrize("splits", [(0, 0), (1, 1), (3, 2)])
-def test_shared_prefix_parity(kv, D, Hq, Hkv, prefix, ctx, ql, causal, splits):
-    """Queries of sequences that share their first pages: prefix attended once
-    by all queries packed together, suffixes per sequence, merged; the result
-    matches the oracle (which knows nothing of the sharing) and pa_prefill."""
+@pytest.mark.parametrize("plan", SHARED_PLANS)
+def test_shared_prefix_parity(kv, D, Hq, Hkv, prefix, ctx, ql, causal, plan):
+    """Queries of sequences that share their first pages.  Packed: the q_len = 1
+    rows attend the prefix once, packed together, and their own keys apart,
+    merged, while rows with q_len > 1 take the ordinary pass; plain: the
+    ordinary pass for all.  The result matches the oracle (which knows nothing
+    of the sharing) and pa_prefill."""
     _log(f"shared prefix kv={kv} D={D} Hq={Hq} Hkv={Hkv} prefix={prefix} ctx={ctx} "
-         f"q={ql} causal={causal} splits={splits}")
+         f"q={ql} causal={causal} plan={plan}")
     wl = workloads.small("prefill", kv_dtype=kv, q_dtype="bf16", num_q_heads=Hq,
                          num_kv_heads=Hkv, head_dim=D, ctx_lens=ctx, q_lens=ql, seed=90 + D,
                          shared_prefix=prefix, causal=causal)
     pool, opool = H.device_pool(wl), H.oracle_pool(wl)
     call = wl.calls[0]
-    o, lse = _run_shared(wl, call, pool, prefix, prefix_splits=splits[0],
-                         suffix_splits=splits[1])
+    o, lse = _run_shared(wl, call, pool, prefix, mode=plan[0], prefix_splits=plan[1],
+                         suffix_splits=plan[2], plain_splits=plan[3])
     torch.cuda.synchronize()
     ro, rl = H.oracle_call(opool, wl, call)
     eo, el = H.max_err(o, lse, ro, rl)
@@ -451,22 +460,24 @@ def test_shared_prefix_parity(kv, D, Hq, Hkv, prefix, ctx, ql, causal, splits):
     assert (lse - l2).abs().max().item() <= 1e-3
 
 
-def test_shared_prefix_mixed_step_full_size():
+@pytest.mark.parametrize("mode", [pa.SHARED_AUTO, pa.SHARED_PACKED])
+def test_shared_prefix_mixed_step_full_size(mode):
     """The 16-sequence fp8 mixed step (8 chunks of 256 and 8 decode rows over a
     shared 1024-token prefix) as one shared-prefix call, in the benchmark's
-    configuration, against the oracle on every row."""
-    _log("shared prefix: mixed fp8 16x1536 as one call")
+    configuration (the library's choice) and packed, against the oracle on
+    every row."""
+    _log(f"shared prefix: mixed fp8 16x1536 as one call, mode {mode}")
     wl, opool = _named(5)
     pool = H.device_pool(wl)
     call = workloads.one_call(wl)
-    o, lse = _run_shared(wl, call, pool, wl.shared_prefix)
+    o, lse = _run_shared(wl, call, pool, wl.shared_prefix, mode=mode)
     torch.cuda.synchronize()
     ro, rl = H.oracle_call(opool, wl, call)
     eo, el = H.max_err(o, lse, ro, rl)
     _log(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert eo <= H.TOL["fp8"] and el <= H.TOL["fp8"]
     # repeat: bitwise the same
-    o2, l2 = _run_shared(wl, call, pool, wl.shared_prefix)
+    o2, l2 = _run_shared(wl, call, pool, wl.shared_prefix, mode=mode)
     assert torch.equal(o, o2) and torch.equal(lse, l2)
 
 
@@ -479,14 +490,40 @@ def test_shared_prefix_decode_only_splits_the_prefix():
                          q_lens=(1, 1, 1, 1), seed=97, shared_prefix=4096)
     pool, opool = H.device_pool(wl), H.oracle_pool(wl)
     call = wl.calls[0]
-    sp, ss = pa.shared_prefix_num_splits(4, 8, 32, 1, 4400, 4096, 4)
+    plan = pa.shared_prefix_plan(pool, 4, 32, 1, 4400, 4096, 4, mode=pa.SHARED_PACKED)
+    sp, ss = plan["prefix_splits"], plan["suffix_splits"]
     assert sp > 1
-    o, lse = _run_shared(wl, call, pool, 4096)
+    o, lse = _run_shared(wl, call, pool, 4096, mode=pa.SHARED_PACKED)
     torch.cuda.synchronize()
     ro, rl = H.oracle_call(opool, wl, call)
     eo, el = H.max_err(o, lse, ro, rl)
     _log(f"  splits={sp},{ss} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert eo <= H.TOL["bf16"] and el <= H.TOL["bf16"]
+
+
+def test_shared_prefix_auto_packs_decode_rows_of_a_mixed_batch():
+    """16 decode rows and one 64-token chunk over a 4096-token bf16 prefix: the
+    library packs the decode rows (their prefix reads beyond the first are
+    252 MB) and runs the chunk through the ordinary pass; every row matches the
+    oracle and the plain arrangement."""
+    _log("shared prefix: auto plan on 16 decode rows + 1 chunk")
+    ctx = tuple(4096 + 20 + 7 * i for i in range(16)) + (4096 + 64,)
+    wl = workloads.small("prefill", kv_dtype="bf16", q_dtype="bf16", num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, ctx_lens=ctx, q_lens=(1,) * 16 + (64,),
+                         seed=98, shared_prefix=4096)
+    pool, opool = H.device_pool(wl), H.oracle_pool(wl)
+    call = wl.calls[0]
+    plan = pa.shared_prefix_plan(pool, 17, 32, 64, max(ctx), 4096, 80)
+    assert plan["mode"] == pa.SHARED_PACKED
+    o, lse = _run_shared(wl, call, pool, 4096)
+    torch.cuda.synchronize()
+    ro, rl = H.oracle_call(opool, wl, call)
+    eo, el = H.max_err(o, lse, ro, rl)
+    _log(f"  plan={plan} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= H.TOL["bf16"] and el <= H.TOL["bf16"]
+    o2, l2 = _run_shared(wl, call, pool, 4096, mode=pa.SHARED_PLAIN)
+    assert (o.float() - o2.float()).abs().max().item() <= H.TOL["bf16"]
+    assert (lse - l2).abs().max().item() <= 1e-3
 
 
 @pytest.mark.parametrize("k", [1, 2, 4, 5])
