@@ -453,6 +453,37 @@ def measured_ceilings(pa, dev) -> dict:
     return res
 
 
+def page_pattern_floor(pa, dev, nbytes: float, steps: int, scratch) -> dict:
+    """The decode's read pattern with no arithmetic (pa_probe_page_stream) over
+    about the same volume, spread evenly over 256, 512 or 1024 workgroups (the
+    best of the three), timed like the decode (cache evicted first when the
+    decode's is)."""
+    import torch
+    unit = 1024 * 8192
+    nb = max(unit, int(nbytes) // unit * unit)
+    buf = torch.ones(nb, dtype=torch.uint8, device=dev)
+    out = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+    best = None
+    for blocks in (256, 512, 1024):
+        pa.probe_page_stream(buf, blocks=blocks, out=out)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, steps)):
+            if scratch is not None:
+                scratch.sum(dtype=torch.int64)
+            e0, e1 = FenceFreeEvent(), FenceFreeEvent()
+            e0.record()
+            pa.probe_page_stream(buf, blocks=blocks, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = statistics.median(ts)
+        if best is None or ms < best["ms"]:
+            best = {"bytes": nb, "ms": ms, "gbps": nb / (ms * 1e-3) / 1e9, "workgroups": blocks}
+    del buf
+    return best
+
+
 class FenceFreeEvent:
     """A HIP timing event created with hipEventDisableSystemFence, from the HIP
     runtime torch has loaded.  Its record carries no system-scope release, so
@@ -721,6 +752,11 @@ def main():
                 m = ceil["mfma_fp8_tflops" if r["peak"] == PEAK_FP8_TFLOPS else "mfma_bf16_tflops"]
             r["measured_peak"] = m
             r["frac_measured"] = r["achieved"] / m
+    if not args.no_ceilings:
+        for d in dec:
+            f = page_pattern_floor(pa, dev, d["kv_bytes"], args.steps, scratch)
+            d["page_pattern_floor"] = f
+            d["frac_of_page_pattern_floor"] = (f["ms"] * d["kv_bytes"] / f["bytes"]) / d["ms"]
     if args.one_call:
         for wl in wls:
             if wl.shared_prefix and len(wl.calls) > 1:

@@ -486,7 +486,7 @@ pa_status pa_plan_append(pa_allocator* a, int32_t* block_table, int32_t bt_strid
                          int32_t max_copies, int32_t* num_copies);
 
 /* ------------------------------------------------------------ measurement probes
- * Not part of the attention path.  Two kernels that measure what this GPU
+ * Not part of the attention path.  Kernels that measure what this GPU
  * sustains, so that each attention kernel's rate can be read against a
  * measured ceiling as well as the spec peak (bench.py runs these beside the
  * attention kernels).
@@ -495,6 +495,15 @@ pa_status pa_plan_append(pa_allocator* a, int32_t* block_table, int32_t bt_strid
  *   multiple of 16) is read once with non-temporal loads by `blocks`
  *   workgroups of 256 threads in a grid-stride loop; out (device,
  *   blocks * 256 uint32) receives one XOR per thread of the words it read.
+ * pa_probe_page_stream: the bf16 d = 128 decode's read pattern with no
+ *   arithmetic.  buf is cut into `blocks` equal runs of 8 KiB pages (bytes a
+ *   multiple of blocks * 8192); workgroup i (4 waves) reads run i, each wave
+ *   every fourth page with two pages in flight, a page as a 4 KiB K page
+ *   (16 keys x 64-byte pieces per 16-byte-per-lane load) then a 4 KiB V page
+ *   (8 bytes per lane), the decode kernel's loads.  out (device, blocks * 256
+ *   uint32) receives one XOR per thread.  The time for a volume with the work
+ *   evenly spread: the floor of that pattern, below which a decode that
+ *   streams its pages this way cannot go.
  * pa_probe_mfma: `blocks` workgroups of 4 waves; each wave runs 4 independent
  *   chains of `iters` MFMAs on register operands.  PA_BF16 uses
  *   v_mfma_f32_32x32x16_bf16 (32768 FLOP each), PA_FP8_E4M3
@@ -502,10 +511,13 @@ pa_status pa_plan_append(pa_allocator* a, int32_t* block_table, int32_t bt_strid
  *   each); out (device, blocks * 256 float) receives each thread's sum of its
  *   accumulators.  FLOP per call: blocks * 16 * iters * the instruction's.
  * Errors: PA_ERR_INVALID_ARG for null pointers, bytes 0 or not a multiple of
- * 16, blocks outside [1, 65535], iters < 1; PA_ERR_UNSUPPORTED for another
+ * 16 (of blocks * 8192 for the page stream), blocks outside [1, 65535],
+ * iters < 1; PA_ERR_UNSUPPORTED for another
  * dtype; PA_ERR_LAUNCH when the launch fails.  Stream-ordered on `stream`.
  */
 pa_status pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
+                               void* stream);
+pa_status pa_probe_page_stream(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
                                void* stream);
 pa_status pa_probe_mfma(pa_dtype dtype, float* out, int32_t blocks, int32_t iters, void* stream);
 

@@ -101,6 +101,7 @@ _copy_blocks = _sig("pa_copy_blocks", ctypes.c_int, [_P, _VP, _VP, _I32, _VP])
 _plan_append = _sig("pa_plan_append", ctypes.c_int,
                     [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP])
 _probe_read = _sig("pa_probe_stream_read", ctypes.c_int, [_VP, _SZ, _VP, _I32, _VP])
+_probe_page = _sig("pa_probe_page_stream", ctypes.c_int, [_VP, _SZ, _VP, _I32, _VP])
 _probe_mfma = _sig("pa_probe_mfma", ctypes.c_int, [ctypes.c_int, _VP, _I32, _I32, _VP])
 
 EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes", "pa_write_kv",
@@ -112,7 +113,7 @@ EXPORTED = ["pa_status_string", "pa_abi_version", "pa_write_kv_workspace_bytes",
             "pa_shared_prefix_workspace_bytes", "pa_prefill_shared_prefix",
             "pa_decode_balanced_workspace_bytes", "pa_decode_choose_splits",
             "pa_backward_workspace_bytes", "pa_prefill_backward", "pa_prefill_fp8",
-            "pa_probe_stream_read", "pa_probe_mfma", "pa_decode_noalloc"]
+            "pa_probe_stream_read", "pa_probe_page_stream", "pa_probe_mfma", "pa_decode_noalloc"]
 
 SCRATCH_BYTES = 8 << 20   # PA_SCRATCH_BYTES
 
@@ -565,6 +566,17 @@ def probe_stream_read(buf: torch.Tensor, blocks: int = 2048, out: torch.Tensor |
         out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
     _check(_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), blocks,
                        _stream(stream)), "pa_probe_stream_read")
+    return out
+
+
+def probe_page_stream(buf: torch.Tensor, blocks: int = 256, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Read buf in the decode's page pattern, evenly over `blocks` workgroups
+    (pa_probe_page_stream); returns the per-thread XORs."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    _check(_probe_page(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), blocks,
+                       _stream(stream)), "pa_probe_page_stream")
     return out
 
 

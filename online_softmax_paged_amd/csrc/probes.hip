@@ -1,5 +1,5 @@
-// Measurement probes: a streaming read of a device buffer and MFMA loops on
-// register operands.  They are not part of the attention path; they measure
+// Measurement probes: a streaming read of a device buffer, the same read in
+// the decode's page pattern, and MFMA loops on register operands.  They are not part of the attention path; they measure
 // what this GPU sustains so that each attention kernel's rate can be read
 // against a measured ceiling as well as against the spec peak.
 #include "pa_internal.h"
@@ -16,6 +16,48 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   u32x4 acc = {0, 0, 0, 0};
   for (size_t i = tid; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
   out[tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// The decode's read pattern without its arithmetic: each workgroup (four
+// waves) streams its own run of pages of 8 KiB (a bf16 d = 128 K page of 4 KiB
+// read as 16 keys x 64-byte pieces per 16-byte-per-lane load, then the V page
+// of 4 KiB read 8 bytes per lane), each wave taking every fourth page with two
+// pages in flight, as decode_split_kernel loads them.  All workgroups get the
+// same number of pages, so this is the time that pattern needs for a given
+// volume with the work perfectly balanced.
+__global__ __launch_bounds__(256) void page_stream_kernel(const char* __restrict__ base,
+                                                          int pages_per_wg,
+                                                          uint32_t* __restrict__ out) {
+  constexpr int kRingP = 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, grp = lane >> 4;
+  const char* wg = base + static_cast<size_t>(blockIdx.x) * pages_per_wg * 8192;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int p0 = wave * kRingP; p0 < pages_per_wg; p0 += 4 * kRingP) {
+    u32x4 k[kRingP][4];
+    u32x2 v[kRingP][8];
+#pragma unroll
+    for (int r = 0; r < kRingP; ++r) {
+      const int p = min(p0 + r, pages_per_wg - 1);
+      const char* kp = wg + static_cast<size_t>(p) * 8192;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        k[r][ks] = *reinterpret_cast<const u32x4*>(kp + (c * 128 + ks * 32 + grp * 8) * 2);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        v[r][db] = *reinterpret_cast<const u32x2*>(kp + 4096 + ((db * 16 + c) * 16 + grp * 4) * 2);
+    }
+#pragma unroll
+    for (int r = 0; r < kRingP; ++r) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc ^= k[r][ks];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        acc.x ^= v[r][db].x;
+        acc.y ^= v[r][db].y;
+      }
+    }
+  }
+  out[static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
 // Each wave: four independent accumulator chains of iters MFMAs each.
@@ -70,6 +112,18 @@ pa_status pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int
     return PA_ERR_INVALID_ARG;
   stream_read_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const u32x4*>(buf), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_probe_page_stream(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
+                               void* stream) {
+  if (!buf || !out || blocks < 1 || blocks > 65535 || bytes == 0 ||
+      bytes % (static_cast<size_t>(blocks) * 8192) != 0 ||
+      bytes / (static_cast<size_t>(blocks) * 8192) > (1u << 30))
+    return PA_ERR_INVALID_ARG;
+  const int pages = static_cast<int>(bytes / (static_cast<size_t>(blocks) * 8192));
+  page_stream_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const char*>(buf), pages, out);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -34,3 +34,24 @@ def test_fence_free_events_time_like_torch_events():
     floor_ms = 10 * 2 * (256 << 20) / 8e12 * 1e3
     assert f >= floor_ms and t >= floor_ms
     assert 0.85 <= f / t <= 1.15
+
+
+def test_page_stream_probe_reads_every_word_once():
+    """The decode-pattern probe bench.py uses as the decode's floor reads each
+    32-bit word of its buffer exactly once: the XOR of its per-thread results
+    equals the XOR of the whole buffer (2 workgroups x 8 pages and 3 x 16)."""
+    import online_softmax_paged_amd as pa
+    g = torch.Generator().manual_seed(5)
+    for blocks, pages in ((2, 8), (3, 16)):
+        host = torch.randint(-2**31, 2**31 - 1, (blocks * pages * 8192 // 4,), generator=g,
+                             dtype=torch.int64).to(torch.int32)
+        buf = host.cuda()
+        out = pa.probe_page_stream(buf, blocks=blocks)
+        torch.cuda.synchronize()
+        want = 0
+        for w in host.tolist():
+            want ^= w & 0xffffffff
+        got = 0
+        for w in out.cpu().tolist():
+            got ^= w & 0xffffffff
+        assert got == want, (blocks, pages)
