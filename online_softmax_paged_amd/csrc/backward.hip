@@ -215,32 +215,37 @@ __global__ __launch_bounds__(256) void bwd_pages_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (sequence, KV head, 128 keys); wave w owns keys
-// 32w..32w+31 of them, K and V of its keys held as MFMA operands.  The query
-// tiles (32 rows) that see any of the keys are staged in LDS for all four
-// waves: Q and dO row-major, Q^T and dO^T feature-major, D and LSE*log2(e).
-// Staging is by buffer loads straight into LDS (dma16) into two stages, so
-// the next tile moves while one is multiplied: wave w moves one of the four
-// operand tiles (its lanes' source offsets chosen so that the linear LDS
-// writes land in the swizzled layout), waves 0 and 1 also the row statistics.
+// dK, dV: one workgroup per (sequence, KV head, 32 * NW keys); wave w owns
+// keys 32w..32w+31 of them, K and V of its keys held as MFMA operands.  The
+// query tiles (32 rows) that see any of the keys are staged in LDS for all
+// the waves: Q and dO row-major, Q^T and dO^T feature-major, D and
+// LSE*log2(e).  Staging is by buffer loads straight into LDS (dma16) into two
+// stages, so the next tile moves while one is multiplied: waves w and w + 4
+// share operand tile w % 4 (their lanes' source offsets chosen so that the
+// linear LDS writes land in the swizzled layout), waves 0 and 1 also move the
+// row statistics.
 template <int D>
 struct RowsStage {
   uint16_t q[kBT * D], d[kBT * D], qt[kBT * D], dt[kBT * D];
   float lse2[256], delta[256];  // one 1 KiB load each; the first 32 floats used
 };
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
   constexpr int NI = kBT * D * 2 / 1024;  // 1 KiB loads per operand tile
-  // d = 128: one stage of query tiles, and V of the workgroup's 128 keys in
-  // LDS, each lane keeping its own key's operands there (written and read by
-  // that lane only), which leaves the registers for two waves per SIMD.
-  // d = 64 fits two waves with V in registers and two stages.
+  constexpr int KW = kBT * NW;            // keys per workgroup
+  constexpr int NP = NW / 4;              // waves moving each operand tile
+  static_assert(NW % 4 == 0 && NI % NP == 0, "operand tiles split evenly over the waves");
+  // d = 128: V of the workgroup's keys in LDS, each lane keeping its own
+  // key's operands there (written and read by that lane only), which leaves
+  // the registers for two waves per SIMD; 8 waves (256 keys) share each staged
+  // query tile, in two stages (132 KiB of LDS, one workgroup per CU).  d = 64
+  // keeps V in registers.
   constexpr bool kVL = D == 128;
-  constexpr int NS = kVL ? 1 : 2;
+  constexpr int NS = 2;
   __shared__ RowsStage<D> sm[NS];
-  __shared__ uint16_t vsm[kVL ? 4 * kBT * D : 8];
+  __shared__ uint16_t vsm[kVL ? NW * kBT * D : 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   die_task(pair, y);
   const int b = pair / Hkv, g = pair % Hkv;
   const int ctx = clamp_ctx(a, b);
-  const int k0 = y * 128;
+  const int k0 = y * KW;
   if (k0 >= ctx) return;
   const int q0 = a.cu_q_lens[b], qlen = a.cu_q_lens[b + 1] - q0;
   const int nrows = qlen * G, pos_base = ctx - qlen;
@@ -281,17 +286,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-  // per-lane source offsets of this wave's loads (the same for every tile)
-  uint32_t voff[NI];
+  // per-lane source offsets of this wave's loads (the same for every tile):
+  // operand tile ot = wave % 4, its 1 KiB loads part * NI / NP onwards
+  const int ot = wave % 4, part = wave / 4;
+  constexpr int NL = NI / NP;
+  uint32_t voff[NL];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int il = 0; il < NL; ++il) {
+    const int i = part * NL + il;
     const int m = i * 64 + lane;  // 16-byte slot of the operand tile
-    if (wave < 2) {               // row tile: slot m holds chunk pos of row r
+    if (ot < 2) {                 // row tile: slot m holds chunk pos of row r
       const int r = m / CPR, pos = m % CPR, j = pos ^ (r % CPR);
-      voff[i] = static_cast<uint32_t>(((r / G) * Hq + (r % G)) * D * 2 + j * 16);
+      voff[il] = static_cast<uint32_t>(((r / G) * Hq + (r % G)) * D * 2 + j * 16);
     } else {                      // col tile: half c, feature d, 8-row chunk
       const int c = m / (D * 2), w2 = m % (D * 2), d = w2 / 2, e = (w2 % 2) ^ ((d >> 3) & 1);
-      voff[i] = static_cast<uint32_t>((d * a.lpad + 16 * c + 8 * e) * 2);
+      voff[il] = static_cast<uint32_t>((d * a.lpad + 16 * c + 8 * e) * 2);
     }
   }
   const int64_t rowbase = (static_cast<int64_t>(g) * B + b) * a.lpad;
@@ -303,18 +312,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const void* src;
     int32_t nb;
     uint32_t lds;
-    if (wave < 2) {
+    if (ot < 2) {
       const int t0 = R0 / G;
-      src = (wave == 0 ? a.q : a.dout) + (static_cast<int64_t>(q0 + t0) * Hq + g * G) * D;
+      src = (ot == 0 ? a.q : a.dout) + (static_cast<int64_t>(q0 + t0) * Hq + g * G) * D;
       nb = max(0, min(qlen - t0, kBT / G)) * Hq * D * 2;  // the tile's tokens; past the sequence: 0
-      lds = lds_address(wave == 0 ? st.q : st.d);
+      lds = lds_address(ot == 0 ? st.q : st.d);
     } else {
-      src = (wave == 2 ? a.qt : a.dot) + colbase + R0;
+      src = (ot == 2 ? a.qt : a.dot) + colbase + R0;
       nb = col_bytes;
-      lds = lds_address(wave == 2 ? st.qt : st.dt);
+      lds = lds_address(ot == 2 ? st.qt : st.dt);
     }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(src, nb, voff[i], lds + i * 1024);
+    for (int il = 0; il < NL; ++il) dma16(src, nb, voff[il], lds + (part * NL + il) * 1024);
     if (wave < 2)
       dma16((wave == 0 ? a.lse2 : a.delta) + rowbase + R0, kBT * 4, lane * 16,
             lds_address(wave == 0 ? st.lse2 : st.delta));
@@ -328,22 +337,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // a query row R (token R / G) sees this lane's key when R >= lo_row
   const int lo_row = a.causal ? (key - pos_base) * G : INT_MIN;
   const bool key_ok = key < ctx;
-  if (!kVL && tile0 < n_tiles) stage_tile(n_tiles - 1, 0);
+  // this wave's first key; tiles wholly before it (causal) or a wave with no
+  // key in the context skip the arithmetic and only stage
+  const int wkey0 = k0 + kBT * wave;
+  const int wave_lo_row = a.causal ? (wkey0 - pos_base) * G : INT_MIN;
+  const bool wave_keys = wkey0 < ctx;
+  if (tile0 < n_tiles) stage_tile(n_tiles - 1, 0);
   wait_vmcnt<0>();
   for (int it = n_tiles - 1; it >= tile0; --it) {
     const int R0 = it * kBT;
-    int s = 0;
-    if constexpr (kVL) {
-      __syncthreads();  // every wave is done with the tile before
-      stage_tile(it, 0);
-      wait_vmcnt<0>();
-      __syncthreads();  // tile it has landed
-    } else {
-      s = (n_tiles - 1 - it) & 1;
-      __syncthreads();  // tile it has landed; the stage of the tile before is free
-      if (it > tile0) stage_tile(it - 1, s ^ 1);
-    }
+    const int s = (n_tiles - 1 - it) & 1;
+    __syncthreads();  // tile it has landed; the stage of the tile before is free
+    if (it > tile0) stage_tile(it - 1, s ^ 1);
     const RowsStage<D>& st = sm[s];
+    if (!wave_keys || R0 + kBT - 1 < wave_lo_row) {
+      wait_vmcnt<0>();
+      continue;
+    }
 
     // S and dP for (query rows x this lane's key)
     f32x16 sv = {}, dp = {};
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_read<D>(st.qt, d, c, half), sb, dk[db], 0, 0, 0);
       }
     }
-    if constexpr (!kVL) wait_vmcnt<0>();  // this wave's loads of the next tile are in LDS
+    wait_vmcnt<0>();  // this wave's loads of the next tile are in LDS
   }
 
   // write this lane's key: dK token-major, dV feature-major (the pool's layouts)
@@ -574,7 +584,9 @@ hipError_t launch_backward_d(const BwdArgs& a, hipStream_t st) {
   const int max_pages = (a.max_ctx_len + kPage - 1) / kPage;
   bwd_rows_kernel<D><<<dim3((a.lpad + 63) / 64, a.num_kv_heads, a.num_seqs), 256, 0, st>>>(a);
   bwd_pages_kernel<D><<<dim3(max_pages, a.num_kv_heads, a.num_seqs), 256, 0, st>>>(a);
-  bwd_dkdv_kernel<D><<<dim3(a.num_seqs * a.num_kv_heads, (a.max_ctx_len + 127) / 128), 256, 0, st>>>(a);
+  constexpr int NW = D == 128 ? 8 : 4;
+  bwd_dkdv_kernel<D, NW><<<dim3(a.num_seqs * a.num_kv_heads, (a.max_ctx_len + 32 * NW - 1) / (32 * NW)),
+                           64 * NW, 0, st>>>(a);
   bwd_dq_kernel<D><<<dim3(a.num_seqs * a.num_kv_heads, (a.max_q_len * G + 127) / 128), 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -102,6 +102,66 @@ def test_backward_prefill_1x2048_sampled_against_oracle():
     _check(wl, call, do, dq, dk, dv)
 
 
+def test_backward_bench_shape_sampled_pairs_against_oracle():
+    """The benchmark's backward, 4 x 4096 causal, 32 q / 8 KV heads, d=128, in
+    the launch bench.py times (forward unsplit, dO from its seed).  Every
+    gradient is finite; three (sequence, KV head) pairs -- first, middle and
+    last -- are checked whole against the dense float64 backward of
+    oracle/backward.py: dQ of their 4 x 4096 query rows and dK, dV of all
+    their 256 pages (every workgroup of those pairs, both kernels)."""
+    from oracle import gather_kv
+    from oracle.backward import attention_backward_dense
+    _log("backward 4 x 4096 (bench shape), sampled pairs")
+    wl = workloads.causal_prefill_bf16()
+    call = wl.calls[0]
+    pool = H.device_pool(wl)
+    dc = H.DeviceCall(wl, call)
+    o, lse = pa.prefill(pool, dc.q, dc.cu_q_lens, dc.ctx_lens, dc.block_table, wl.scale,
+                        max_q_len=dc.max_q_len, max_ctx_len=dc.max_ctx_len, num_splits=1)
+    T, Hq, D = dc.q.shape
+    do = workloads.upstream_grad(call, D, Hq, seed=2024)
+    dq = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+    dk = torch.zeros(pool.k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(pool.v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.backward_workspace_bytes(pool, len(call.q_lens), Hq, dc.max_q_len),
+                     dtype=torch.uint8, device="cuda")
+    pa.prefill_backward(pool, dc.q, o, lse, do.cuda(), dc.cu_q_lens, dc.ctx_lens, dc.block_table,
+                        wl.scale, max_q_len=dc.max_q_len, max_ctx_len=dc.max_ctx_len, dq=dq,
+                        dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    dq, dk, dv = (x.cpu().to(torch.float64).numpy() for x in (dq, dk, dv))
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    opool = H.oracle_pool(wl)
+    G = Hq // wl.num_kv_heads
+    qf, dof = call.q.to(torch.float64).numpy(), do.to(torch.float64).numpy()
+    cu, bt = call.cu_q_lens.tolist(), call.block_table.numpy()
+    for b, g in ((0, 0), (2, 3), (3, 7)):
+        c = int(call.ctx_lens[b])
+        q0, q1 = cu[b], cu[b + 1]
+        pos = c - (q1 - q0) + np.arange(q1 - q0)
+        K, V = gather_kv(opool, bt[b], c, g)
+        dk_ref, dv_ref = np.zeros((c, D)), np.zeros((c, D))
+        dq_err = dq_max = 0.0
+        for h in range(g * G, (g + 1) * G):
+            rq, rk, rv = attention_backward_dense(qf[q0:q1, h], K, V, dof[q0:q1, h], wl.scale,
+                                                  pos, True)
+            dq_err = max(dq_err, float(np.abs(dq[q0:q1, h] - rq).max()))
+            dq_max = max(dq_max, float(np.abs(rq).max()))
+            dk_ref += rk
+            dv_ref += rv
+        pages = bt[b][np.arange(c) // 16]
+        slots = np.arange(c) % 16
+        dk_got = dk[pages, g, slots, :]
+        dv_got = dv[pages, g, :, slots]
+        dk_err = float(np.abs(dk_got - dk_ref).max())
+        dv_err = float(np.abs(dv_got - dv_ref).max())
+        bars = [REL * max(1.0, m) for m in (dq_max, float(np.abs(dk_ref).max()),
+                                             float(np.abs(dv_ref).max()))]
+        _log(f"  pair ({b},{g}): dQ {dq_err:.2e} (bar {bars[0]:.2e}) dK {dk_err:.2e} "
+             f"(bar {bars[1]:.2e}) dV {dv_err:.2e} (bar {bars[2]:.2e})")
+        assert dq_err <= bars[0] and dk_err <= bars[1] and dv_err <= bars[2]
+
+
 def _random_cases(n, seed):
     import random
     rng = random.Random(seed)
