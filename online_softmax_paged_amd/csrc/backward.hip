@@ -427,20 +427,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per (sequence, KV head, 128 query rows), wave w owning
-// rows 32w..32w+31 with its Q and dO rows as MFMA operands; the key tiles
-// (32 keys, two pages) it sees are staged in LDS, two stages deep: K and V
-// token-major, K feature-major -- six page groups, each wave moving one
-// instruction's worth of every group.
+// dQ: one workgroup per (sequence, KV head, 32 * NW query rows), wave w
+// owning rows 32w..32w+31 with its Q and dO rows as MFMA operands; the key
+// tiles (32 keys, two pages) it sees are staged in LDS, two stages deep: K
+// and V token-major, K feature-major -- six page groups, the waves sharing
+// their loads evenly.
 template <int D>
 struct KeysStage {
   uint16_t k[kBT * D], v[kBT * D], kt[kBT * D];
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
   constexpr int PER = kPage * D * 2 / 1024;  // 1 KiB loads per page group
+  constexpr int RW = kBT * NW;               // query rows per workgroup
   __shared__ KeysStage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int nrows = qlen * G;
   // row blocks from the last one down: under a causal mask the last rows see
   // the most keys, so the longest tasks start first
-  const int W0 = (gridDim.y - 1 - y) * 128;
+  const int W0 = (gridDim.y - 1 - y) * RW;
   if (W0 >= nrows) return;
   const int ctx = clamp_ctx(a, b);
   const int pos_base = ctx - qlen;
@@ -481,15 +482,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  // this wave's instruction of each of the six page groups: K page 0/1 and V
-  // page 0/1 (row layout), K^T page 0/1 (col layout); PER instructions per
-  // group, instruction u = i*4 + wave
-  constexpr int NI = 6 * PER / 4;
+  // this wave's instructions of the six page groups: K page 0/1 and V page
+  // 0/1 (row layout), K^T page 0/1 (col layout); PER instructions per group,
+  // instruction u = i*NW + wave
+  static_assert(6 * PER % NW == 0, "page groups split evenly over the waves");
+  constexpr int NI = 6 * PER / NW;
   uint32_t voff[NI], ldso[NI];
   int grp[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int u = i * 4 + wave, gr = u / PER, sub = u % PER;
+    const int u = i * NW + wave, gr = u / PER, sub = u % PER;
     const int m = sub * 64 + lane, p = gr & 1;
     grp[i] = gr;
     if (gr < 4) {
@@ -502,12 +504,23 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       ldso[i] = static_cast<uint32_t>(p * D * 32 + m * 16);
     }
   }
+  // page ids, 64 pages (32 key tiles) per lane vector, read out with readlane:
+  // one table read per 32 tiles instead of one wait per tile
+  int id_chunk = -1;
+  int32_t idv = -1;
+  auto page_at = [&](int pg) -> int32_t {
+    if ((pg >> 6) != id_chunk) {
+      id_chunk = pg >> 6;
+      idv = page_id(a, b, 64 * id_chunk + lane, n_pages);
+    }
+    return __builtin_amdgcn_readlane(idv, pg & 63);
+  };
   auto stage_tile = [&](int kt, int s) {
     int64_t chunk[2];
     int32_t nb[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int32_t ph = page_id(a, b, 2 * kt + p, n_pages);
+      const int32_t ph = page_at(2 * kt + p);
       chunk[p] = (static_cast<int64_t>(ph < 0 ? 0 : ph) * Hkv + g) * (kPage * D);
       nb[p] = ph < 0 ? 0 : kPage * D * 2;
     }
@@ -522,7 +535,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  const int t_last = min(W0 + 127, nrows - 1) / G;
+  const int t_last = min(W0 + RW - 1, nrows - 1) / G;
   const int kmax = a.causal ? min(ctx, pos_base + t_last + 1) : ctx;
   const int n_kt = (kmax + kBT - 1) / kBT;
   if (n_kt > 0) stage_tile(0, 0);
@@ -534,6 +547,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();  // tile kt has landed; the stage of tile kt-1 is free
     if (kt + 1 < n_kt) stage_tile(kt + 1, s ^ 1);
     const KeysStage<D>& st = sm[s];
+    if (__all(kt * kBT > key_lim)) {  // no key of the tile seen by a row of this wave
+      wait_vmcnt<0>();
+      continue;
+    }
 
     // S^T and dP^T for (keys x this lane's row)
     f32x16 sv = {}, dp = {};
@@ -587,7 +604,8 @@ hipError_t launch_backward_d(const BwdArgs& a, hipStream_t st) {
   constexpr int NW = D == 128 ? 8 : 4;
   bwd_dkdv_kernel<D, NW><<<dim3(a.num_seqs * a.num_kv_heads, (a.max_ctx_len + 32 * NW - 1) / (32 * NW)),
                            64 * NW, 0, st>>>(a);
-  bwd_dq_kernel<D><<<dim3(a.num_seqs * a.num_kv_heads, (a.max_q_len * G + 127) / 128), 256, 0, st>>>(a);
+  bwd_dq_kernel<D, NW><<<dim3(a.num_seqs * a.num_kv_heads, (a.max_q_len * G + 32 * NW - 1) / (32 * NW)),
+                         64 * NW, 0, st>>>(a);
   return hipGetLastError();
 }
 
