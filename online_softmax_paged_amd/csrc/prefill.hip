@@ -1166,10 +1166,10 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     const int8_t* kb = reinterpret_cast<const int8_t*>(stg);
     auto scores = [&](auto two) {
 #pragma unroll
-      for (int beta = 0; beta < 2; ++beta) {
-        const int key = 32 * ((col >> 2) & 1) + 16 * beta + 4 * (col >> 3) + (col & 3);
+      for (int ks = 0; ks < D / 64; ++ks) {
 #pragma unroll
-        for (int ks = 0; ks < D / 64; ++ks) {
+        for (int beta = 0; beta < 2; ++beta) {  // the two blocks' chains interleaved
+          const int key = 32 * ((col >> 2) & 1) + 16 * beta + 4 * (col >> 3) + (col & 3);
           const int c0 = 4 * ks + 2 * half;
           const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + (key * CK + (c0 ^ fp8_ksw<D>(key))) * 16);
           const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + (key * CK + ((c0 + 1) ^ fp8_ksw<D>(key))) * 16);
