@@ -937,6 +937,12 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
   const int tile = n_tiles - 1 - y / S, split = y % S;
   const int TQ = 128 / G;
 
+  // The prologue's memory reads overlap instead of chaining: the block ids of
+  // pages 0..127 load with the sequence lengths, the first tiles' DMA goes
+  // out as soon as they arrive, and Q and the page scales load beside it.
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int32_t id_raw0 = lane < a.bt_stride ? bt[lane] : -1;
+  const int32_t id_raw1 = 64 + lane < a.bt_stride ? bt[64 + lane] : -1;
   const int q0 = a.cu_q_lens[b];
   const int qlen = a.cu_q_lens[b + 1] - q0;
   int ctx = a.ctx_lens[b];
@@ -961,27 +967,30 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
   const int qpos = pos_base + tt;
   const int key_lim = a.causal ? min(qpos, ctx - 1) : ctx - 1;
   const int64_t qrow = static_cast<int64_t>(q0 + (row_ok ? tt : 0)) * Hq + g * G + hg;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
 
-  // largest V page scale among this workgroup's keys (the P.V reference)
-  float sv_max = 0.f;
+  // Q's raw bf16 row parts: this lane holds features 64ks + 32*half .. +31
+  u32x4 raw[D / 64][4];
   {
-    const int p1 = min(n_pages, n_kt * (KT / kPage));
-    for (int p = kt_begin * (KT / kPage) + lane; p < p1; p += 64) {
-      const int32_t id = bt[p];
-      if (id >= 0 && id < a.num_blocks) sv_max = fmaxf(sv_max, a.v_scale[id]);
-    }
-    sv_max = wave_max(sv_max);
-    if (!(sv_max > 0.f)) sv_max = 1.f;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        raw[ks][c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 64 * ks + 32 * half + 8 * c)
+                            : u32x4{0, 0, 0, 0};
   }
 
   // Lane vectors of 64 pages (16 tiles), read out per tile with readlane: the
   // DMA side keeps the page ids two tiles ahead; the compute side keeps its
   // own ids, K scales, and log2 and inverse of the P code factors.
-  const float p_scale = 112.f / sv_max;  // weights <= 4 reach codes <= 448
+  auto valid_id = [&](int p, int32_t id) -> int32_t {
+    return p < n_pages && id >= 0 && id < a.num_blocks ? id : -1;
+  };
+  const int32_t id0 = valid_id(lane, id_raw0), id1 = valid_id(64 + lane, id_raw1);
   auto page_id = [&](int p) -> int32_t {
-    const int32_t id = p < n_pages ? bt[p] : -1;
-    return id >= 0 && id < a.num_blocks ? id : -1;
+    if (p < 64) return id0;
+    if (p < 128) return id1;  // p = 64 + lane
+    return valid_id(p, p < n_pages ? bt[p] : -1);
   };
   int d_chunk = -1;
   int32_t d_idv = -1;
@@ -997,6 +1006,7 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
   int c_chunk = -1;
   int32_t idv = -1;
   float ksv = 0.f, lvsv = -INFINITY, ivsv = 0.f;
+  float p_scale = 1.f;
   auto load_chunk = [&](int c) {  // compute side
     c_chunk = c;
     const int32_t id = page_id(64 * c + lane);
@@ -1038,24 +1048,39 @@ void prefill_fp8mma_kernel(AttnArgs a, int n_tiles) {
     dma_tile(kt_begin + 1, lds0 + STAGE);
   }
 
+  // largest V page scale among this workgroup's keys (the P.V reference)
+  float sv_max = 0.f;
+  {
+    const int p0 = kt_begin * (KT / kPage), p1 = min(n_pages, n_kt * (KT / kPage));
+    const int32_t ids[2] = {id0, id1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int p = 64 * h + lane;
+      if (p >= p0 && p < p1 && ids[h] >= 0) sv_max = fmaxf(sv_max, a.v_scale[ids[h]]);
+    }
+    for (int p = max(p0, 128) + lane; p < p1; p += 64) {
+      const int32_t id = valid_id(p, bt[p]);
+      if (id >= 0) sv_max = fmaxf(sv_max, a.v_scale[id]);
+    }
+    sv_max = wave_max(sv_max);
+    if (!(sv_max > 0.f)) sv_max = 1.f;
+  }
+  p_scale = 112.f / sv_max;  // weights <= 4 reach codes <= 448
+  if (kt_begin < n_kt) load_chunk((4 * kt_begin) >> 6);
+
   // Q row split in two E4M3 parts: this lane holds features 64ks + 32*half .. +31
   i32x8 qc[D / 64], ql[D / 64];
   float sq;
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
-    u32x4 raw[D / 64][4];
     float amax = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        raw[ks][c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 64 * ks + 32 * half + 8 * c)
-                            : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[ks][c][k] << 16)),
                                    fabsf(__builtin_bit_cast(float, raw[ks][c][k] & 0xffff0000u))));
-      }
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     sq = amax > 0.f ? amax / 448.f : 1.f;
     const float inv = amax > 0.f ? 448.f / amax : 1.f;
