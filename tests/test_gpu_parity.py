@@ -322,6 +322,10 @@ FP8MMA_CASES = [
     (64, 4, 4, (257, 33), None, True),                   # G = 1
     (128, 16, 2, (150, 90), (150, 17), True),            # G = 8
     (128, 8, 2, (20, 5, 70, 64), None, True),            # rows that see 1 .. 70 keys
+    # block tables past 64 and 128 pages: the page-id lane vectors' later
+    # chunks, and with 3 splits a split whose first tile lies in chunk 1
+    (128, 8, 2, (2600, 2100), (64, 1), True),
+    (64, 4, 2, (2200,), (40,), False),
 ]
 
 
