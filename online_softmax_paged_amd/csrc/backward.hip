@@ -141,20 +141,31 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < D * 8; idx += 256) {
-    const int d = idx / 8, e = idx % 8;
+  // a feature pair (2 dp, 2 dp + 1) of 8 rows per lane: 8 four-byte LDS reads
+  // give two 16-byte chunks of the transposed rows
+  for (int idx = tid; idx < (D / 2) * 8; idx += 256) {
+    const int dp = idx / 8, e = idx % 8;
     const int R = R0 + 8 * e;
     if (R >= a.lpad) continue;
-    u32x4 wq, wd;
+    uint32_t q2[8], d2[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      q2[k] = *reinterpret_cast<const uint32_t*>(sq + (8 * e + k) * LD + 2 * dp);
+      d2[k] = *reinterpret_cast<const uint32_t*>(sd + (8 * e + k) * LD + 2 * dp);
+    }
+    u32x4 q0, q1, w0, w1;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int r = 8 * e + 2 * k;
-      wq[k] = static_cast<uint32_t>(sq[r * LD + d]) | (static_cast<uint32_t>(sq[(r + 1) * LD + d]) << 16);
-      wd[k] = static_cast<uint32_t>(sd[r * LD + d]) | (static_cast<uint32_t>(sd[(r + 1) * LD + d]) << 16);
+      q0[k] = (q2[2 * k] & 0xffffu) | (q2[2 * k + 1] << 16);
+      q1[k] = (q2[2 * k] >> 16) | (q2[2 * k + 1] & 0xffff0000u);
+      w0[k] = (d2[2 * k] & 0xffffu) | (d2[2 * k + 1] << 16);
+      w1[k] = (d2[2 * k] >> 16) | (d2[2 * k + 1] & 0xffff0000u);
     }
-    const int64_t off = ((static_cast<int64_t>(g) * B + b) * D + d) * a.lpad + R;
-    *reinterpret_cast<u32x4*>(a.qt + off) = wq;
-    *reinterpret_cast<u32x4*>(a.dot + off) = wd;
+    const int64_t off = ((static_cast<int64_t>(g) * B + b) * D + 2 * dp) * a.lpad + R;
+    *reinterpret_cast<u32x4*>(a.qt + off) = q0;
+    *reinterpret_cast<u32x4*>(a.qt + off + a.lpad) = q1;
+    *reinterpret_cast<u32x4*>(a.dot + off) = w0;
+    *reinterpret_cast<u32x4*>(a.dot + off + a.lpad) = w1;
   }
 }
 
