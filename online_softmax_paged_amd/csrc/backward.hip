@@ -202,26 +202,34 @@ __global__ __launch_bounds__(256) void bwd_pages_kernel(BwdArgs a) {
     *reinterpret_cast<u32x4*>(sv + d * 24 + e * 8) = w;
   }
   __syncthreads();
-  for (int idx = tid; idx < 2 * D; idx += 256) {  // kfm chunk (feature d, slots 8e..8e+7)
-    const int d = idx / 2, e = idx % 2;
-    u32x4 w;
+  // each lane reads a pair of features (or of slots) with 4-byte LDS reads
+  // and writes the two transposed 16-byte chunks they hold
+  auto split2 = [](const uint32_t (&x)[8], u32x4& lo, u32x4& hi) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int s = e * 8 + 2 * k;
-      w[k] = static_cast<uint32_t>(sk[s * (D + 8) + d]) |
-             (static_cast<uint32_t>(sk[(s + 1) * (D + 8) + d]) << 16);
+      lo[k] = (x[2 * k] & 0xffffu) | (x[2 * k + 1] << 16);
+      hi[k] = (x[2 * k] >> 16) | (x[2 * k + 1] & 0xffff0000u);
     }
-    *reinterpret_cast<u32x4*>(a.kfm + chunk + d * kPage + e * 8) = w;
+  };
+  for (int idx = tid; idx < D; idx += 256) {  // kfm chunks (features 2dp, 2dp+1; slots 8e..8e+7)
+    const int dp = idx / 2, e = idx % 2;
+    uint32_t x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = *reinterpret_cast<const uint32_t*>(sk + (e * 8 + k) * (D + 8) + 2 * dp);
+    u32x4 w0, w1;
+    split2(x, w0, w1);
+    *reinterpret_cast<u32x4*>(a.kfm + chunk + (2 * dp) * kPage + e * 8) = w0;
+    *reinterpret_cast<u32x4*>(a.kfm + chunk + (2 * dp + 1) * kPage + e * 8) = w1;
   }
-  for (int idx = tid; idx < kPage * CPR; idx += 256) {  // vtm chunk (slot s, features 8c..8c+7)
-    const int s = idx / CPR, c = idx % CPR;
-    u32x4 w;
+  for (int idx = tid; idx < (kPage / 2) * CPR; idx += 256) {  // vtm chunks (slots 2sp, 2sp+1; features 8c..8c+7)
+    const int sp = idx / CPR, c = idx % CPR;
+    uint32_t x[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int d = c * 8 + 2 * k;
-      w[k] = static_cast<uint32_t>(sv[d * 24 + s]) | (static_cast<uint32_t>(sv[(d + 1) * 24 + s]) << 16);
-    }
-    *reinterpret_cast<u32x4*>(a.vtm + chunk + s * D + c * 8) = w;
+    for (int k = 0; k < 8; ++k) x[k] = *reinterpret_cast<const uint32_t*>(sv + (c * 8 + k) * 24 + 2 * sp);
+    u32x4 w0, w1;
+    split2(x, w0, w1);
+    *reinterpret_cast<u32x4*>(a.vtm + chunk + (2 * sp) * D + c * 8) = w0;
+    *reinterpret_cast<u32x4*>(a.vtm + chunk + (2 * sp + 1) * D + c * 8) = w1;
   }
 }
 
